@@ -1,0 +1,18 @@
+"""CPU oracle of the zero-computation-expert MoE layer.
+
+TEST INFRASTRUCTURE, not part of the product.  Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py`` may import or run
+anything in this package.  It shares no code, header, table or helper with the GPU
+library in ``mixture_experts_layer_router_amd``; the two meet only through the seeded
+inputs of the ``inputs`` package.
+
+Modules:
+  moe         vectorised fp64 oracle: router, biased top-K, load, permutation, SwiGLU
+              experts, combine (the reference every GPU result is compared against)
+  bruteforce  scalar pure-Python formulation for tiny inputs (pins moe)
+  dense       dense-masked formulation of the combine (pins moe's permute/combine)
+  tune_routing_inputs
+              offline script: tunes the zero-expert bias shift and lists the tokens
+              whose selection scores are too close to order reliably; writes
+              inputs/routing_tables.json
+"""
