@@ -1,0 +1,237 @@
+"""Benchmark of the zero-computation-expert MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+                    [--no-decode] [--no-cpu-baseline] [--calib-copy]
+
+One step = one lc_moe_forward (router, permutation, grouped SwiGLU FFN, combine) over the
+workload's resident inputs.  Prints ONE JSON line.  value = tokens/s of the whole layer
+(inputs and weights already in HBM).  Per-stage times come from HIP events recorded by
+lc_moe_forward_staged on the launch stream inside the timed region.
+
+roofline: the dominant kernel is the gate/up grouped GEMM (two thirds of the FFN FLOPs
+and weight bytes); achieved = its algorithmic FLOPs per launch (4*d*I per FFN pick) over
+its mean event-timed duration, against the dense bf16 MFMA peak.
+decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
+(gate/up + down) is bound by streaming the weights of the experts that received at least
+one token; reported against the HBM peak.
+cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer tokens/s and % of bf16 MFMA peak (prefill) / % HBM peak (decode)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def setup(wl, dev):
+    import torch
+    import mixture_experts_layer_router_amd as lm
+    from inputs.generate import expert_weights, routing_inputs
+    ri = routing_inputs(wl)
+    w = expert_weights(wl, dev)
+    x = ri.x_torch(dev)
+    wr, b = ri.w_router_torch(dev), ri.bias_torch(dev)
+    shape = lm.make_shape(wl.T, wl.d, wl.N, wl.Z, wl.K, wl.I, lm.BF16 if wl.dtype == "bf16" else lm.F32)
+    ws = lm.workspace_for(shape, dev)
+    outs = dict(y=torch.empty_like(x),
+                idx=torch.empty((wl.T, wl.K), dtype=torch.int32, device=dev),
+                gate=torch.empty((wl.T, wl.K), dtype=torch.float32, device=dev),
+                load=torch.empty(wl.E, dtype=torch.int32, device=dev))
+    wts = lm._weights(wr, b, w["gate"], w["up"], w["down"])
+    torch.cuda.synchronize()
+    return dict(ri=ri, w=w, x=x, wr=wr, b=b, shape=shape, ws=ws, outs=outs, wts=wts)
+
+
+def run_steps(lm, st, steps, warmup):
+    """Warm up, then time exactly `steps` forwards; returns (total_ms, per-stage ms lists)."""
+    import torch
+    o = st["outs"]
+
+    def fwd(events=None):
+        lm.lc_moe_forward_staged(st["shape"], st["x"], st["wts"], o["y"], o["idx"], o["gate"],
+                                 o["load"], st["ws"], stage_events=events)
+
+    for _ in range(warmup):
+        fwd()
+    nst = lm.NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        fwd(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(stop)
+    stages = {lm.stage_name(s): [evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)]
+              for s in range(nst)}
+    return total, stages
+
+
+def cpu_baseline(st, wl, max_ffn_rows=1536):
+    """Oracle timed on the host: route, permute and combine over all T tokens; the SwiGLU
+    FFN on the rows of the first FFN experts (about max_ffn_rows rows), scaled to nnz."""
+    from inputs.generate import weights_f64
+    from oracle import moe as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = len(os.sched_getaffinity(0))
+    ri = st["ri"]
+    x = ri.x_f64()
+    wr = ri.w_router.astype(np.float64)
+    t0 = time.perf_counter()
+    idx, gate, _ = orc.route(x, wr, ri.bias, wl.K)
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    offsets, perm_token, slot_row = orc.permute(idx, wl.N)
+    t_perm = time.perf_counter() - t0
+    nnz = int(offsets[-1])
+    t_ffn, rows, experts = 0.0, 0, 0
+    y_perm = np.zeros((nnz, wl.d))
+    for e in range(wl.N):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        wg, wu, wd = (weights_f64(st["w"][k][e]) for k in ("gate", "up", "down"))
+        t0 = time.perf_counter()
+        y_perm[r0:r1] = orc.swiglu_expert(x[perm_token[r0:r1]], wg, wu, wd)
+        t_ffn += time.perf_counter() - t0
+        rows += r1 - r0
+        experts += 1
+        if rows >= max_ffn_rows:
+            break
+    t0 = time.perf_counter()
+    orc.combine(x, y_perm, idx, gate, slot_row, wl.N)
+    t_comb = time.perf_counter() - t0
+    t_ffn_scaled = t_ffn * nnz / max(rows, 1)
+    total = t_route + t_perm + t_ffn_scaled + t_comb
+    return {"value": wl.T / total, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle; routing, permutation and combine over all {wl.T} tokens; "
+                       f"SwiGLU FFN on the {rows} rows of the first {experts} FFN experts "
+                       f"(of {nnz} FFN rows), FFN time scaled by {nnz}/{rows}; "
+                       f"route {t_route:.2f}s permute {t_perm:.2f}s ffn {t_ffn:.2f}s "
+                       f"(scaled {t_ffn_scaled:.1f}s) combine {t_comb:.2f}s; "
+                       f"elementwise numpy on 1 thread, BLAS on {blas_threads}")}
+
+
+def decode_runs(lm, dev, steps, warmup):
+    import torch
+    from inputs import configs
+    res = []
+    for T in configs.DECODE_T:
+        for share in configs.DECODE_SHARES:
+            wl = configs.decode(T, share)
+            st = setup(wl, dev)
+            total, stages = run_steps(lm, st, steps, warmup)
+            load = st["outs"]["load"].cpu().numpy()
+            touched = int((load[:wl.N] > 0).sum())
+            wbytes = touched * 3 * wl.I * wl.d * 2
+            ffn_ms = float(np.mean(stages["gate_up"]) + np.mean(stages["down"]))
+            gbs = wbytes / (ffn_ms * 1e-3) / 1e9
+            res.append({"T": T, "zero_share_pct": share, "ms_per_step": total / steps,
+                        "tokens_per_s": T * steps / (total * 1e-3), "touched_experts": touched,
+                        "ffn_rows": int(load[:wl.N].sum()), "ffn_ms": ffn_ms,
+                        "ffn_weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                        "stages_ms": {k: float(np.mean(v)) for k, v in stages.items()}})
+            log(f"decode T={T} share={share}%: {total / steps:.3f} ms/step, FFN {ffn_ms:.3f} ms, "
+                f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+            del st
+            torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 4 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer runs on a single MI355X here and this build "
+              f"has no multi-GPU path; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_router_amd as lm
+    from inputs import configs
+
+    dev = torch.device("cuda:0")
+    wl = configs.get(args.workload)
+    log(f"workload: {wl.description}")
+    st = setup(wl, dev)
+    log("inputs resident")
+    total, stages = run_steps(lm, st, args.steps, args.warmup)
+    ms = total / args.steps
+    load = st["outs"]["load"].cpu().numpy()
+    nnz = int(load[:wl.N].sum())
+    touched = int((load[:wl.N] > 0).sum())
+    st_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    gu_flops = 4.0 * wl.d * wl.I * nnz
+    dn_flops = 2.0 * wl.d * wl.I * nnz
+    gu_tflops = gu_flops / (st_ms["gate_up"] * 1e-3) / 1e12
+    ffn_ms = st_ms["gate_up"] + st_ms["down"]
+    ffn_tflops = (gu_flops + dn_flops) / (ffn_ms * 1e-3) / 1e12
+    wbytes = touched * 3 * wl.I * wl.d * 2
+    log(f"{ms:.3f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in st_ms.items()})}")
+    log(f"gate_up {gu_tflops:.0f} TFLOP/s ({gu_tflops / MFMA_BF16_PEAK_TFLOPS:.1%}); FFN {ffn_tflops:.0f} "
+        f"TFLOP/s ({ffn_tflops / MFMA_BF16_PEAK_TFLOPS:.1%}); weights {wbytes / ffn_ms / 1e6:.0f} GB/s")
+
+    if args.calib_copy:
+        a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        bcp = torch.empty_like(a)
+        for _ in range(3):
+            bcp.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcp
+
+    result = {
+        "metric": METRIC, "value": wl.T * args.steps / (total * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": wl.description, "T": wl.T, "d": wl.d, "N": wl.N, "Z": wl.Z,
+                   "K": wl.K, "I": wl.I, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "ffn_bf16_kernel<0> (gate/up + SwiGLU)",
+                     "achieved": gu_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": gu_flops, "launch_ms": st_ms["gate_up"]},
+        "ffn": {"rows": nnz, "touched_experts": touched, "ms": ffn_ms, "TFLOPs": ffn_tflops,
+                "mfma_frac": ffn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
+        "stages_ms": st_ms,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(st, wl)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = decode_runs(lm, dev, max(5, args.steps), args.warmup)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

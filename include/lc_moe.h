@@ -1,0 +1,158 @@
+/*
+ * lc_moe -- forward pass of a mixture-of-experts layer with zero-computation experts,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (LongCat-Flash article, itouyu.top; Italian kqgmpj.cn; French dhxrcw.cn;
+ * section "Zero-computation experts"): the expert pool holds N FFN experts and Z
+ * zero-computation experts that return their input unchanged.  A softmax router R
+ * scores token x_t over all N+Z experts, p_t = softmax(W_r x_t).  An expert-specific bias
+ * b_i, adjusted from recent expert usage and decoupled from the training loss (same
+ * section, bias paragraph), is added to the scores only to choose the K experts of each
+ * token; the chosen experts are combined with the unbiased scores as gates:
+ *
+ *   S_t  = K largest p_t,i + b_i  (equal values: lower index first)
+ *   y_t  = sum_{i in S_t, i <  N} p_t,i * W_down,i (silu(W_gate,i x_t) * (W_up,i x_t))
+ *        + sum_{i in S_t, i >= N} p_t,i * x_t
+ *
+ * so a token runs between 0 and K FFN experts.  The FFN experts are SwiGLU blocks
+ * without biases, silu(a) = a / (1 + exp(-a)).  Experts 0..N-1 are FFN experts,
+ * N..N+Z-1 are zero-computation experts.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers, row-major and contiguous, aligned to 16
+ *     bytes; the caller owns them and keeps them alive until the stream work completes.
+ *     The library allocates no device memory, never synchronises the stream, keeps no
+ *     pointer after return and holds no mutable global state.
+ *   - dtype LC_MOE_BF16: x, the three expert weight tensors and y are bf16;
+ *     LC_MOE_F32: they are fp32.  The router weight W_r, the bias b and the gates are
+ *     always fp32; arithmetic accumulates in fp32 (the router logits exactly as an fp32
+ *     dot product of x with W_r).
+ *   - Host-side checks run before anything is enqueued.  On any error status nothing is
+ *     enqueued and every output is left untouched.  Device faults surface at the
+ *     caller's next synchronisation.  NaN or Inf inputs are outside the contract.
+ *   - Results are deterministic: two calls with the same inputs give bitwise equal
+ *     outputs (no floating-point atomics anywhere).
+ *   - Limits: T, d, N, K, I >= 1; Z >= 0; K <= N+Z; N+Z <= 4096; N <= 2048;
+ *     T*K < 2^31; d and I multiples of 8 for bf16 (4 for fp32).
+ */
+#ifndef LC_MOE_H
+#define LC_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LC_MOE_OK = 0,
+  LC_MOE_E_NULLPTR = 1,   /* a required pointer is NULL                                */
+  LC_MOE_E_SHAPE = 2,     /* a size is out of range (see the limits above)             */
+  LC_MOE_E_DTYPE = 3,     /* dtype is neither LC_MOE_F32 nor LC_MOE_BF16              */
+  LC_MOE_E_ALIGN = 4,     /* a pointer is not 16-byte aligned                          */
+  LC_MOE_E_WORKSPACE = 5, /* workspace smaller than lc_moe_workspace_size()            */
+  LC_MOE_E_DEVICE = 6     /* a HIP call or kernel launch reported an error             */
+} lc_moe_status;
+
+typedef enum { LC_MOE_F32 = 0, LC_MOE_BF16 = 1 } lc_moe_dtype;
+
+/* Layer shape (host struct).  T tokens of width d; N FFN experts with SwiGLU
+ * intermediate width I; Z zero-computation experts; K experts chosen per token. */
+typedef struct {
+  int32_t T, d, N, Z, K, I;
+  int32_t dtype; /* lc_moe_dtype */
+} lc_moe_shape;
+
+/* Layer weights (host struct holding device pointers). */
+typedef struct {
+  const float* w_router; /* [N+Z][d] fp32: router R                                      */
+  const float* bias;     /* [N+Z]    fp32: expert bias b, used for selection only         */
+  const void* w_gate;    /* [N][I][d] dtype: SwiGLU gate projection of each FFN expert    */
+  const void* w_up;      /* [N][I][d] dtype: SwiGLU up projection                        */
+  const void* w_down;    /* [N][d][I] dtype: SwiGLU down projection                      */
+} lc_moe_weights;
+
+/* Stages of lc_moe_forward, in launch order (names from lc_moe_stage_name). */
+#define LC_MOE_NUM_STAGES 5 /* route, permute, gate_up, down, combine */
+
+/* Bytes of device workspace every entry point below needs for this shape (0 if the
+ * shape is invalid).  The same workspace may be reused by consecutive calls on one
+ * stream; calls that overlap in time need separate workspaces.  Pure host arithmetic. */
+size_t lc_moe_workspace_size(const lc_moe_shape* shape);
+
+/* Router and biased top-K (section "Zero-computation experts": softmax router R over
+ * the whole N+Z pool, bias added for the choice only).
+ *   x          [T][d] dtype        tokens
+ *   w_router   [N+Z][d] fp32       router weights
+ *   bias       [N+Z] fp32          expert bias
+ *   topk_idx   [T][K] int32 (out)  chosen experts of each token, ordered by
+ *                                  (p + b descending, expert index ascending)
+ *   topk_gate  [T][K] fp32 (out)   their unbiased softmax probabilities p
+ * p is computed in fp32: logits as fp32 dot products, max-subtracted exp, sum, divide;
+ * the selection compares fp32 p + b. */
+lc_moe_status lc_moe_route(const lc_moe_shape* shape, const void* x, const float* w_router,
+                           const float* bias, int32_t* topk_idx, float* topk_gate,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Expert usage counts, the statistic a bias controller consumes (bias paragraph of the
+ * same section: the bias follows recent expert usage).
+ *   topk_idx       [T][K] int32       picks (values in 0..N+Z-1)
+ *   load           [N+Z] int32 (out)  number of picks of each expert; sums to T*K
+ *   ffn_per_token  [T] int32 (out)    number of FFN experts (index < N) among each
+ *                                     token's picks, 0..K; may be NULL */
+lc_moe_status lc_moe_expert_load(const lc_moe_shape* shape, const int32_t* topk_idx,
+                                 int32_t* load, int32_t* ffn_per_token, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Token permutation into expert-contiguous rows.  Zero-computation picks get no row:
+ * they need no compute (section "Zero-computation experts").
+ *   x            [T][d] dtype
+ *   topk_idx     [T][K] int32
+ *   ffn_offsets  [N+1] int32 (out)   exclusive prefix sum of the FFN experts' loads;
+ *                                    ffn_offsets[N] = nnz, the number of FFN picks
+ *   perm_token   [T*K] int32 (out)   token of each row; rows of expert e are
+ *                                    ffn_offsets[e]..ffn_offsets[e+1]-1, tokens
+ *                                    ascending; entries from nnz on are untouched
+ *   slot_row     [T][K] int32 (out)  row of pick (t,k), -1 for a zero-computation pick
+ *   x_perm       [T*K][d] dtype (out) x_perm[r] = x[perm_token[r]] for r < nnz; may be NULL
+ *   load         [N+Z] int32 (out)   as lc_moe_expert_load; may be NULL */
+lc_moe_status lc_moe_permute(const lc_moe_shape* shape, const void* x, const int32_t* topk_idx,
+                             int32_t* ffn_offsets, int32_t* perm_token, int32_t* slot_row,
+                             void* x_perm, int32_t* load, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Whole layer: route -> permute -> grouped SwiGLU FFN over the FFN picks only ->
+ * combine, where the combine adds, in the order of each token's picks, g * (expert
+ * output) for FFN picks and g * x_t for zero-computation picks, in fp32, rounding y
+ * once to dtype (nearest even).  Intermediates (gated activations, expert outputs) are
+ * stored in dtype.  One stream, no host synchronisation, capturable into a HIP graph.
+ *   x          [T][d] dtype
+ *   weights    host struct of device pointers (see lc_moe_weights)
+ *   y          [T][d] dtype (out)
+ *   topk_idx   [T][K] int32 (out, may be NULL)
+ *   topk_gate  [T][K] fp32 (out, may be NULL)
+ *   load       [N+Z] int32 (out, may be NULL) */
+lc_moe_status lc_moe_forward(const lc_moe_shape* shape, const void* x,
+                             const lc_moe_weights* weights, void* y, int32_t* topk_idx,
+                             float* topk_gate, int32_t* load, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* lc_moe_forward with instrumentation: when stage_events is not NULL it holds
+ * LC_MOE_NUM_STAGES + 1 events created by the caller; event 0 is recorded on the stream
+ * before the first stage and event i+1 after stage i.  Same results as lc_moe_forward. */
+lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
+                                    const lc_moe_weights* weights, void* y, int32_t* topk_idx,
+                                    float* topk_gate, int32_t* load, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* stage_events);
+
+/* Static strings; never NULL. */
+const char* lc_moe_status_str(lc_moe_status status);
+const char* lc_moe_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LC_MOE_H */

@@ -181,4 +181,4 @@ def expert_weights(wl: Workload, device="cpu") -> dict:
 def weights_f64(t) -> np.ndarray:
     """Exact fp64 copy of a (cpu or device) fp32/bf16 torch tensor, for the oracle."""
     import torch
-    return t.detach().to("cpu", torch.float64).numpy()
+    return t.detach().cpu().to(torch.float64).numpy()

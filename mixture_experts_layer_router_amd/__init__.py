@@ -1,0 +1,236 @@
+"""Python binding of lc_moe (liblc_moe.so): argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module converts torch tensors to
+device pointers and the current torch stream to a hipStream_t, checks tensor
+dtype/shape/device, and turns an error status into an exception.  torch is used only for
+device memory and streams.  Importing raises if the library has not been built
+(``python -m mixture_experts_layer_router_amd.build``); there is no fallback path.
+
+Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
+``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``,
+``lc_moe_workspace_size``); ``route``, ``expert_load``, ``permute`` and ``forward``
+allocate the outputs and a workspace with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblc_moe.so")
+
+# torch must be loaded first: its wheel ships its own HIP runtime with the same soname
+# (libamdhip64.so.7).  Loaded in this order, liblc_moe.so binds to that runtime and the
+# process holds one HIP runtime; the other order would load two.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m mixture_experts_layer_router_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16 = 0, 1
+NUM_STAGES = 5
+STATUS = {0: "ok", 1: "E_NULLPTR", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN", 5: "E_WORKSPACE",
+          6: "E_DEVICE"}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("Z", ctypes.c_int32), ("K", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+_SIG = {
+    "lc_moe_workspace_size": (_sz, [ctypes.POINTER(Shape)]),
+    "lc_moe_route": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lc_moe_expert_load": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lc_moe_permute": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]),
+    "lc_moe_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights), _vp,
+                                      _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lc_moe_forward_staged": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights),
+                                             _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "lc_moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "lc_moe_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+EXPORTED = tuple(_SIG)
+
+
+class LcMoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({_lib.lc_moe_status_str(status).decode()})")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LcMoeError(status, where)
+
+
+def status_str(status: int) -> str:
+    return _lib.lc_moe_status_str(status).decode()
+
+
+def stage_name(i: int) -> str:
+    return _lib.lc_moe_stage_name(i).decode()
+
+
+def make_shape(T, d, N, Z, K, I, dtype) -> Shape:
+    if not isinstance(dtype, int):
+        import torch
+        dtype = BF16 if dtype == torch.bfloat16 else F32 if dtype == torch.float32 else -1
+    return Shape(T, d, N, Z, K, I, dtype)
+
+
+def lc_moe_workspace_size(shape: Shape) -> int:
+    return int(_lib.lc_moe_workspace_size(ctypes.byref(shape)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ---- low-level: same names and argument order as the C-ABI ------------------------------
+
+def lc_moe_route(shape, x, w_router, bias, topk_idx, topk_gate, workspace, stream=None):
+    _check(_lib.lc_moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias),
+                             _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), _nbytes(workspace),
+                             _stream(stream)), "lc_moe_route")
+
+
+def lc_moe_expert_load(shape, topk_idx, load, ffn_per_token, workspace, stream=None):
+    _check(_lib.lc_moe_expert_load(ctypes.byref(shape), _ptr(topk_idx), _ptr(load),
+                                   _ptr(ffn_per_token), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream)), "lc_moe_expert_load")
+
+
+def lc_moe_permute(shape, x, topk_idx, ffn_offsets, perm_token, slot_row, x_perm, load,
+                   workspace, stream=None):
+    _check(_lib.lc_moe_permute(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(ffn_offsets),
+                               _ptr(perm_token), _ptr(slot_row), _ptr(x_perm), _ptr(load),
+                               _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "lc_moe_permute")
+
+
+def _weights(w_router, bias, w_gate, w_up, w_down) -> Weights:
+    return Weights(w_router.data_ptr(), bias.data_ptr(), w_gate.data_ptr(), w_up.data_ptr(),
+                   w_down.data_ptr())
+
+
+def lc_moe_forward(shape, x, weights: Weights, y, topk_idx, topk_gate, load, workspace,
+                   stream=None):
+    _check(_lib.lc_moe_forward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
+                               _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _ptr(workspace),
+                               _nbytes(workspace), _stream(stream)), "lc_moe_forward")
+
+
+def lc_moe_forward_staged(shape, x, weights: Weights, y, topk_idx, topk_gate, load, workspace,
+                          stream=None, stage_events=None):
+    arr = None
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
+    _check(_lib.lc_moe_forward_staged(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
+                                      _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _ptr(workspace),
+                                      _nbytes(workspace), _stream(stream),
+                                      ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None),
+           "lc_moe_forward_staged")
+
+
+# ---- convenience wrappers: allocate outputs with torch, then call the C entry point -----
+
+def _shape_of(x, N, Z, K, I):
+    T, d = x.shape
+    return make_shape(T, d, N, Z, K, I, x.dtype)
+
+
+def workspace_for(shape: Shape, device):
+    import torch
+    n = lc_moe_workspace_size(shape)
+    if n == 0:
+        raise LcMoeError(2, "lc_moe_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(x, w_router, bias, K, N, workspace=None):
+    """(topk_idx int32 [T,K], topk_gate fp32 [T,K])."""
+    import torch
+    E = w_router.shape[0]
+    shape = _shape_of(x, N, E - N, K, 8)
+    ws = workspace if workspace is not None else workspace_for(shape, x.device)
+    idx = torch.empty((x.shape[0], K), dtype=torch.int32, device=x.device)
+    gate = torch.empty((x.shape[0], K), dtype=torch.float32, device=x.device)
+    lc_moe_route(shape, x, w_router, bias, idx, gate, ws)
+    return idx, gate
+
+
+def expert_load(topk_idx, N, E, workspace=None, d=8, dtype=BF16):
+    """(load int32 [E], ffn_per_token int32 [T])."""
+    import torch
+    T, K = topk_idx.shape
+    shape = make_shape(T, d, N, E - N, K, 8, dtype)
+    ws = workspace if workspace is not None else workspace_for(shape, topk_idx.device)
+    load = torch.empty(E, dtype=torch.int32, device=topk_idx.device)
+    ffn = torch.empty(T, dtype=torch.int32, device=topk_idx.device)
+    lc_moe_expert_load(shape, topk_idx, load, ffn, ws)
+    return load, ffn
+
+
+def permute(x, topk_idx, N, E, with_x_perm=True, workspace=None):
+    """dict(ffn_offsets, perm_token, slot_row, x_perm, load)."""
+    import torch
+    T, K = topk_idx.shape
+    shape = make_shape(T, x.shape[1], N, E - N, K, 8, x.dtype)
+    ws = workspace if workspace is not None else workspace_for(shape, x.device)
+    dev = x.device
+    out = dict(ffn_offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
+               perm_token=torch.full((T * K,), -7, dtype=torch.int32, device=dev),
+               slot_row=torch.empty((T, K), dtype=torch.int32, device=dev),
+               x_perm=torch.empty((T * K, x.shape[1]), dtype=x.dtype, device=dev) if with_x_perm else None,
+               load=torch.empty(E, dtype=torch.int32, device=dev))
+    lc_moe_permute(shape, x, topk_idx, out["ffn_offsets"], out["perm_token"], out["slot_row"],
+                   out["x_perm"], out["load"], ws)
+    return out
+
+
+def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_events=None):
+    """dict(y, topk_idx, topk_gate, load); x [T,d]; w_gate/w_up [N,I,d]; w_down [N,d,I]."""
+    import torch
+    N, I, _ = w_gate.shape
+    E = w_router.shape[0]
+    shape = _shape_of(x, N, E - N, K, I)
+    ws = workspace if workspace is not None else workspace_for(shape, x.device)
+    T, dev = x.shape[0], x.device
+    y = torch.empty_like(x)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    load = torch.empty(E, dtype=torch.int32, device=dev)
+    wts = _weights(w_router, bias, w_gate, w_up, w_down)
+    if stage_events is None:
+        lc_moe_forward(shape, x, wts, y, idx, gate, load, ws)
+    else:
+        lc_moe_forward_staged(shape, x, wts, y, idx, gate, load, ws, stage_events=stage_events)
+    return dict(y=y, topk_idx=idx, topk_gate=gate, load=load)

@@ -1,0 +1,81 @@
+// Fused combine: y_t = sum over the token's picks, in pick order, of g * E_i(x_t), where
+// E_i(x_t) is the FFN expert's output row for an FFN pick and x_t itself for a
+// zero-computation pick (LongCat-Flash article, itouyu.top, section "Zero-computation
+// experts": the identity expert returns its input).  fp32 accumulation, one rounding to
+// the output dtype.  One workgroup per token; 16-byte vector loads along d.
+#include "common.h"
+
+namespace lcm {
+
+__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ ybuf,
+                                                           const int32_t* __restrict__ slot_row,
+                                                           const float* __restrict__ gate,
+                                                           bf16_t* __restrict__ y, int d, int K) {
+  const int t = blockIdx.x;
+  const bf16_t* xt = x + size_t(t) * d;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const float g = gate[size_t(t) * K + k];
+      const int r = slot_row[size_t(t) * K + k];
+      const bf16_t* src = r >= 0 ? ybuf + size_t(r) * d : xt;
+      float v[8];
+      load8(src + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f2bf(acc[2 * i]) | (uint32_t(f2bf(acc[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(y + size_t(t) * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ x,
+                                                          const float* __restrict__ ybuf,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ gate,
+                                                          float* __restrict__ y, int d, int K) {
+  const int t = blockIdx.x;
+  const float* xt = x + size_t(t) * d;
+  for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < K; ++k) {
+      const float g = gate[size_t(t) * K + k];
+      const int r = slot_row[size_t(t) * K + k];
+      const float4 v = *reinterpret_cast<const float4*>((r >= 0 ? ybuf + size_t(r) * d : xt) + c);
+      acc.x = fmaf(g, v.x, acc.x);
+      acc.y = fmaf(g, v.y, acc.y);
+      acc.z = fmaf(g, v.z, acc.z);
+      acc.w = fmaf(g, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(y + size_t(t) * d + c) = acc;
+  }
+}
+
+hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,
+                          const int32_t* slot_row, const float* gate, void* y, hipStream_t st) {
+  if (s.dtype == LC_MOE_BF16) {
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(s.T), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(ybuf), slot_row,
+                       gate, static_cast<bf16_t*>(y), s.d, s.K);
+  } else {
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(s.T), dim3(256), 0, st,
+                       static_cast<const float*>(x), static_cast<const float*>(ybuf), slot_row,
+                       gate, static_cast<float*>(y), s.d, s.K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lcm

@@ -1,0 +1,121 @@
+// Internal definitions shared by the lc_moe HIP sources (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lc_moe.h"
+
+namespace lcm {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMaxE = 4096;     // N + Z limit (router registers, histogram LDS)
+constexpr int kMaxN = 2048;     // N limit (permutation bitmask LDS)
+constexpr int kTokBlock = 256;  // tokens per permutation block
+
+// M-tile height (rows of one expert) of the grouped FFN kernels.
+constexpr int kBmBf16 = 128;
+constexpr int kBmF32 = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// One M-tile of the grouped FFN: rows row0..row0+rows-1 of expert `expert`;
+// first_tile is the index of that expert's first M-tile.
+struct MTile {
+  int expert, row0, rows, first_tile;
+};
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct WsPlan {
+  size_t logits, idx, gate, block_counts, block_base, load, offsets, mtiles, n_mtiles,
+      perm_token, slot_row, hbuf, ybuf, total;
+  int nblocks;  // token blocks of the permutation
+  int bm;       // M-tile height for this dtype
+  int mt_max;   // capacity of the M-tile list
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsPlan plan_workspace(const lc_moe_shape& s) {
+  WsPlan p{};
+  const size_t T = s.T, K = s.K, E = size_t(s.N) + s.Z, N = s.N;
+  const size_t es = s.dtype == LC_MOE_BF16 ? 2 : 4;
+  p.nblocks = int((T + kTokBlock - 1) / kTokBlock);
+  p.bm = s.dtype == LC_MOE_BF16 ? kBmBf16 : kBmF32;
+  const size_t tk = T * K;
+  size_t mt = N + (tk + p.bm - 1) / p.bm;
+  if (mt > tk) mt = tk;
+  p.mt_max = int(mt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  p.logits = take(T * E * 4);
+  p.idx = take(tk * 4);
+  p.gate = take(tk * 4);
+  p.block_counts = take(size_t(p.nblocks) * E * 4);
+  p.block_base = take(size_t(p.nblocks) * N * 4);
+  p.load = take(E * 4);
+  p.offsets = take((N + 1) * 4);
+  p.mtiles = take(mt * sizeof(MTile));
+  p.n_mtiles = take(4);
+  p.perm_token = take(tk * 4);
+  p.slot_row = take(tk * 4);
+  p.hbuf = take(tk * size_t(s.I) * es);
+  p.ybuf = take(tk * size_t(s.d) * es);
+  p.total = o;
+  return p;
+}
+
+// ---- launchers (host functions defined in the .hip files) ------------------------------
+
+// Router logits L[T][E] = x W_r^T (fp32 result).
+hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
+                                float* logits, hipStream_t st);
+// Softmax over E, biased top-K; writes idx [T][K] and gate [T][K].
+hipError_t launch_router_topk(const lc_moe_shape& s, const float* logits, const float* bias,
+                              int32_t* idx, float* gate, hipStream_t st);
+
+// Per-block expert histogram (+ per-token FFN count when ffn_cnt != nullptr).
+hipError_t launch_histogram(const lc_moe_shape& s, const int32_t* idx, int32_t* block_counts,
+                            int32_t* ffn_cnt, int nblocks, hipStream_t st);
+// Column sums -> load [E]; offsets [N+1]; per-(block, expert) row bases; M-tile list.
+hipError_t launch_scan(const lc_moe_shape& s, const int32_t* block_counts, int nblocks,
+                       int32_t* load, int32_t* offsets, int32_t* block_base, MTile* mtiles,
+                       int32_t* n_mtiles, int bm, hipStream_t st);
+// Stable scatter: slot_row [T][K], perm_token [nnz].
+hipError_t launch_scatter(const lc_moe_shape& s, const int32_t* idx, const int32_t* block_base,
+                          int nblocks, int32_t* slot_row, int32_t* perm_token, hipStream_t st);
+// x_perm[r] = x[perm_token[r]] for r < offsets[N].
+hipError_t launch_gather_rows(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
+                              const int32_t* offsets, void* x_perm, hipStream_t st);
+// Copy n int32 values on the device (kernel, capturable).
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t st);
+
+// Grouped SwiGLU FFN over the FFN picks.
+hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
+                              const void* w_gate, const void* w_up, void* hbuf,
+                              const MTile* mtiles, const int32_t* offsets,
+                              const int32_t* n_mtiles, int mt_max, hipStream_t st);
+hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
+                           void* ybuf, const MTile* mtiles, const int32_t* offsets,
+                           const int32_t* n_mtiles, int mt_max, hipStream_t st);
+
+// y_t = sum_k g_tk * (FFN row or x_t), k ascending, fp32 accumulation.
+hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,
+                          const int32_t* slot_row, const float* gate, void* y, hipStream_t st);
+
+}  // namespace lcm

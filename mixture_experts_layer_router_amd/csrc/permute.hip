@@ -1,0 +1,226 @@
+// Expert load histogram, prefix scan and stable scatter of the FFN picks into
+// expert-contiguous rows.  Zero-computation picks (index >= N) are counted in the load
+// but get no row: they need no compute (LongCat-Flash article, itouyu.top, section
+// "Zero-computation experts"); the load histogram is the "recent expert usage" signal
+// the bias adjustment of that section consumes.
+//
+// Order: rows of expert e are ffn_offsets[e] .. ffn_offsets[e+1]-1 with tokens ascending.
+// Tokens are cut into blocks of 256; a block's rank of token t for expert e is
+//   (picks of e in earlier blocks) + (picks of e by earlier waves of the block)
+//   + popcount(64-lane mask of e in t's wave, lanes below t),
+// all integer, so the result is independent of thread timing.
+#include "common.h"
+
+namespace lcm {
+
+__global__ __launch_bounds__(256) void histogram_kernel(const int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ block_counts,
+                                                        int32_t* __restrict__ ffn_cnt, int T,
+                                                        int K, int E, int N) {
+  __shared__ int cnt[kMaxE];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int t = b * kTokBlock + tid;
+  if (t < T) {
+    int f = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+        atomicAdd(&cnt[e], 1);  // integer: exact whatever the order
+        f += e < N;
+      }
+    }
+    if (ffn_cnt) ffn_cnt[t] = f;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) block_counts[size_t(b) * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ block_counts,
+                                                    int nblocks, int E, int N,
+                                                    int32_t* __restrict__ load,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ block_base,
+                                                    MTile* __restrict__ mtiles,
+                                                    int32_t* __restrict__ n_mtiles, int bm) {
+  __shared__ int tot[kMaxN];
+  __shared__ int part[1024], part2[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int s = 0;
+    for (int b = 0; b < nblocks; ++b) s += block_counts[size_t(b) * E + e];
+    load[e] = s;
+    if (e < N) tot[e] = s;
+  }
+  __syncthreads();
+  // exclusive scans over the N FFN experts of rows and of M-tiles: thread tid owns the
+  // consecutive experts [tid*per, tid*per + per)
+  const int per = (N + 1023) / 1024;
+  int rs = 0, ms = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) {
+      rs += tot[e];
+      ms += (tot[e] + bm - 1) / bm;
+    }
+  }
+  part[tid] = rs;
+  part2[tid] = ms;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= o ? part[tid - o] : 0;
+    const int c = tid >= o ? part2[tid - o] : 0;
+    __syncthreads();
+    part[tid] += a;
+    part2[tid] += c;
+    __syncthreads();
+  }
+  int r = tid > 0 ? part[tid - 1] : 0;
+  int m = tid > 0 ? part2[tid - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) {
+      offsets[e] = r;
+      const int rows = tot[e];
+      const int nt = (rows + bm - 1) / bm;
+      for (int j = 0; j < nt; ++j) {
+        MTile mt;
+        mt.expert = e;
+        mt.row0 = r + j * bm;
+        mt.rows = min(bm, rows - j * bm);
+        mt.first_tile = m;
+        mtiles[m + j] = mt;
+      }
+      r += rows;
+      m += nt;
+    }
+  }
+  if (tid == 1023) {
+    offsets[N] = part[1023];
+    *n_mtiles = part2[1023];
+  }
+  __syncthreads();
+  // per-(block, expert) first row
+  for (int e = tid; e < N; e += 1024) {
+    int run = offsets[e];
+    for (int b = 0; b < nblocks; ++b) {
+      block_base[size_t(b) * N + e] = run;
+      run += block_counts[size_t(b) * E + e];
+    }
+  }
+}
+
+// 256 threads = 4 waves; wave w owns tokens b*256 + w*64 + lane.  Dynamic LDS: 4*N masks.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ block_base,
+                                                      int32_t* __restrict__ slot_row,
+                                                      int32_t* __restrict__ perm_token, int T,
+                                                      int K, int N) {
+  extern __shared__ unsigned long long masks[];  // [4][N]
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4 * N; i += 256) masks[i] = 0ull;
+  __syncthreads();
+  const int t = b * kTokBlock + tid;
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicOr(&masks[w * N + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below_lane = (1ull << lane) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      int row = -1;
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
+        int rank = __popcll(masks[w * N + e] & below_lane);
+        for (int ww = 0; ww < w; ++ww) rank += __popcll(masks[ww * N + e]);
+        row = block_base[size_t(b) * N + e] + rank;
+        perm_token[row] = t;
+      }
+      slot_row[size_t(t) * K + k] = row;
+    }
+  }
+}
+
+// One workgroup per row; rows from offsets[N] on exit at once.
+template <typename V>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const V* __restrict__ x,
+                                                          const int32_t* __restrict__ perm_token,
+                                                          const int32_t* __restrict__ offsets,
+                                                          V* __restrict__ x_perm, int vec_per_row,
+                                                          int N) {
+  const int r = blockIdx.x;
+  if (r >= offsets[N]) return;
+  const V* src = x + size_t(perm_token[r]) * vec_per_row;
+  V* dst = x_perm + size_t(r) * vec_per_row;
+  for (int i = threadIdx.x; i < vec_per_row; i += 256) dst[i] = src[i];
+}
+
+__global__ void copy_i32_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+__global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_histogram(const lc_moe_shape& s, const int32_t* idx, int32_t* block_counts,
+                            int32_t* ffn_cnt, int nblocks, hipStream_t st) {
+  hipLaunchKernelGGL(histogram_kernel, dim3(nblocks), dim3(256), 0, st, idx, block_counts,
+                     ffn_cnt, s.T, s.K, s.N + s.Z, s.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const lc_moe_shape& s, const int32_t* block_counts, int nblocks,
+                       int32_t* load, int32_t* offsets, int32_t* block_base, MTile* mtiles,
+                       int32_t* n_mtiles, int bm, hipStream_t st) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblocks,
+                     s.N + s.Z, s.N, load, offsets, block_base, mtiles, n_mtiles, bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const lc_moe_shape& s, const int32_t* idx, const int32_t* block_base,
+                          int nblocks, int32_t* slot_row, int32_t* perm_token, hipStream_t st) {
+  const size_t lds = size_t(4) * s.N * sizeof(unsigned long long);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), lds, st, idx, block_base,
+                     slot_row, perm_token, s.T, s.K, s.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
+                              const int32_t* offsets, void* x_perm, hipStream_t st) {
+  const size_t row_bytes = size_t(s.d) * (s.dtype == LC_MOE_BF16 ? 2 : 4);
+  const unsigned grid = static_cast<unsigned>(size_t(s.T) * s.K);
+  if (row_bytes % 16 == 0) {
+    hipLaunchKernelGGL(gather_rows_kernel<uint4>, dim3(grid), dim3(256), 0, st,
+                       static_cast<const uint4*>(x), perm_token, offsets,
+                       static_cast<uint4*>(x_perm), int(row_bytes / 16), s.N);
+  } else {
+    hipLaunchKernelGGL(gather_rows_kernel<uint2>, dim3(grid), dim3(256), 0, st,
+                       static_cast<const uint2*>(x), perm_token, offsets,
+                       static_cast<uint2*>(x_perm), int(row_bytes / 8), s.N);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  unsigned grid = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(grid), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  unsigned grid = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(grid), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace lcm

@@ -1,0 +1,305 @@
+// Softmax router R and biased top-K selection (LongCat-Flash article, itouyu.top,
+// section "Zero-computation experts": softmax router over the whole N+Z expert pool;
+// the expert bias only steers which K experts are chosen).
+//
+// Stage 1 (logits): L = x W_r^T with W_r fp32.
+//   bf16 x: bf16 MFMA.  Each fp32 router weight is split exactly into three bf16 parts
+//   w = hi + mid + lo (8 significant bits each; the remainders are exact in fp32), every
+//   product of a bf16 x with a part is exact in fp32, and the MFMA sums them in fp32 --
+//   an fp32 dot product at bf16-MFMA rate (3 MFMAs per fp32 product).
+//   fp32 x: plain fp32 FMA, LDS-tiled.
+// Stage 2 (top-K): one wavefront per token: max, exp, sum and divide in fp32, then K
+//   rounds of a wavefront argmax over s = p + b (ties -> lower index) by shuffles.
+#include "common.h"
+
+namespace lcm {
+
+// ---------------------------------------------------------------------------------------
+// bf16 MFMA logits.  Tile: 128 tokens x 128 experts, K step 32, 256 threads (2x2 waves,
+// 64x64 per wave, v_mfma_f32_32x32x16_bf16).
+// ---------------------------------------------------------------------------------------
+namespace rl {
+constexpr int BM = 128, BN = 128, BK = 32, LDA = BK + 8;  // LDS row: 80 bytes
+}
+
+__device__ __forceinline__ void split3(float w, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
+  hi = f2bf(w);
+  float r1 = w - bf2f(hi);
+  mid = f2bf(r1);
+  float r2 = r1 - bf2f(mid);
+  lo = f2bf(r2);
+}
+
+__global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ logits,
+    int T, int d, int E) {
+  using namespace rl;
+  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[3][BN * LDA];
+
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * BN;
+  const int t0 = blockIdx.y * BM;
+
+  // global -> register prefetch assignment
+  // A: 128 rows x 4 chunks of 8 bf16 -> 2 chunks per thread
+  const bf16_t* a_ptr[2];
+  int a_kc[2], a_row[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int c = tid + i * 256;
+    a_row[i] = c >> 2;
+    a_kc[i] = (c & 3) * 8;
+    int t = t0 + a_row[i];
+    a_ptr[i] = t < T ? x + size_t(t) * d : nullptr;
+  }
+  // B: 128 rows x 8 float4 -> 4 float4 per thread
+  const float* b_ptr[4];
+  int b_k[4], b_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int c = tid + i * 256;
+    b_row[i] = c >> 3;
+    b_k[i] = (c & 7) * 4;
+    int e = e0 + b_row[i];
+    b_ptr[i] = e < E ? wr + size_t(e) * d : nullptr;
+  }
+
+  uint4 ra[2];
+  float4 rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int k = k0 + a_kc[i];
+      ra[i] = (a_ptr[i] && k < d) ? *reinterpret_cast<const uint4*>(a_ptr[i] + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int k = k0 + b_k[i];
+      rb[i] = (b_ptr[i] && k < d) ? *reinterpret_cast<const float4*>(b_ptr[i] + k)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(&As[a_row[i] * LDA + a_kc[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16_t h[4], m[4], l[4];
+      split3(rb[i].x, h[0], m[0], l[0]);
+      split3(rb[i].y, h[1], m[1], l[1]);
+      split3(rb[i].z, h[2], m[2], l[2]);
+      split3(rb[i].w, h[3], m[3], l[3]);
+      int o = b_row[i] * LDA + b_k[i];
+      *reinterpret_cast<uint2*>(&Bs[0][o]) =
+          make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+      *reinterpret_cast<uint2*>(&Bs[1][o]) =
+          make_uint2(m[0] | (uint32_t(m[1]) << 16), m[2] | (uint32_t(m[3]) << 16));
+      *reinterpret_cast<uint2*>(&Bs[2][o]) =
+          make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+    }
+  };
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (d + BK - 1) / BK;
+  load(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+    store();
+    __syncthreads();
+    if (kt + 1 < nk) load((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kk = ks * 16 + lk;
+      bf16x8 a[2], b[3][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + lr) * LDA + kk]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[p][j] = *reinterpret_cast<const bf16x8*>(&Bs[p][(wn * 64 + j * 32 + lr) * LDA + kk]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[p][j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // D layout of 32x32 MFMA: lane holds column (lane & 31), rows 8*(r/4) + 4*(lane/32) + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + wn * 64 + j * 32 + lr;
+      if (e >= E) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < T) logits[size_t(t) * E + e] = acc[i][j][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 logits: 64 tokens x 64 experts per block, K step 16, 4x4 outputs per thread.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wr, float* __restrict__ logits,
+    int T, int d, int E) {
+  __shared__ float Xs[64][17];
+  __shared__ float Ws[64][17];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += 16) {
+    for (int c = tid; c < 64 * 16; c += 256) {
+      int r = c >> 4, k = c & 15;
+      int t = t0 + r, e = e0 + r, kk = k0 + k;
+      Xs[r][k] = (t < T && kk < d) ? x[size_t(t) * d + kk] : 0.f;
+      Ws[r][k] = (e < E && kk < d) ? wr[size_t(e) * d + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(Xs[ty * 4 + i][k], Ws[tx * 4 + j][k], acc[i][j]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
+      if (t < T && e < E) logits[size_t(t) * E + e] = acc[i][j];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Softmax + biased top-K: one wavefront per token, EPL experts per lane
+// (expert e lives in lane e % 64, slot e / 64).
+// ---------------------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ bias,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ gate, int T,
+                                                          int E, int K) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + size_t(t) * E;
+  float v[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+    m = fmaxf(m, v[j]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? expf(v[j] - m) : 0.f;
+    sum += v[j];
+  }
+  // butterfly: a + b == b + a exactly, so every lane ends with the same bits
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  float s[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = v[j] / sum;  // p, IEEE division
+    s[j] = e < E ? v[j] + bias[e] : -INFINITY;
+  }
+  uint64_t taken = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      const bool ok = !((taken >> j) & 1ull) && e < E;
+      if (ok && (s[j] > bv || be == 0x7fffffff)) {  // ascending j: first max keeps lower e
+        bv = s[j];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) {
+      const int j = be >> 6;
+      float p = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < EPL; ++jj)
+        if (jj == j) p = v[jj];
+      taken |= 1ull << j;
+      idx[size_t(t) * K + k] = be;
+      gate[size_t(t) * K + k] = p;
+    }
+  }
+}
+
+hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
+                                float* logits, hipStream_t st) {
+  const int E = s.N + s.Z;
+  if (s.dtype == LC_MOE_BF16) {
+    dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM);
+    hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(x), w_router, logits, s.T, s.d, E);
+  } else {
+    dim3 grid((E + 63) / 64, (s.T + 63) / 64);
+    hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(256), 0, st,
+                       static_cast<const float*>(x), w_router, logits, s.T, s.d, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const lc_moe_shape& s, const float* logits, const float* bias,
+                              int32_t* idx, float* gate, hipStream_t st) {
+  const int E = s.N + s.Z;
+  const int epl = (E + 63) / 64;
+  dim3 grid((s.T + 3) / 4), block(256);
+#define LCM_TOPK(n)                                                                       \
+  hipLaunchKernelGGL(router_topk_kernel<n>, grid, block, 0, st, logits, bias, idx, gate, \
+                     s.T, E, s.K)
+  if (epl <= 2) LCM_TOPK(2);
+  else if (epl <= 4) LCM_TOPK(4);
+  else if (epl <= 8) LCM_TOPK(8);
+  else if (epl <= 16) LCM_TOPK(16);
+  else if (epl <= 32) LCM_TOPK(32);
+  else LCM_TOPK(64);
+#undef LCM_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace lcm

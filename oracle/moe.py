@@ -101,6 +101,18 @@ def swiglu_expert(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: n
     return (silu(G) * U) @ w_down.T
 
 
+def combine(x, y_perm, idx, gate, slot_row, N):
+    """y_t = sum over the token's picks, in pick order, of g times the expert output:
+    the FFN output row for an FFN pick, x_t itself for a zero-computation pick."""
+    y = np.zeros_like(x)
+    for k in range(idx.shape[1]):
+        contrib = x.copy()                           # identity expert: E_i(x) = x
+        is_ffn = idx[:, k] < N
+        contrib[is_ffn] = y_perm[slot_row[is_ffn, k]]
+        y += gate[:, k:k + 1] * contrib
+    return y
+
+
 def moe_forward(x, w_router, bias, experts, N, K, tokens=None):
     """Whole layer forward in fp64.
 
@@ -121,12 +133,7 @@ def moe_forward(x, w_router, bias, experts, N, K, tokens=None):
         if r1 > r0:
             wg, wu, wd = experts(e)
             y_perm[r0:r1] = swiglu_expert(x[perm_token[r0:r1]], wg, wu, wd)
-    y = np.zeros_like(x)
-    for k in range(K):                               # combine in the order of S_t
-        contrib = x.copy()                           # identity expert: E_i(x) = x
-        is_ffn = idx[:, k] < N
-        contrib[is_ffn] = y_perm[slot_row[is_ffn, k]]
-        y += gate[:, k:k + 1] * contrib
+    y = combine(x, y_perm, idx, gate, slot_row, N)
     return dict(idx=idx, gate=gate, y=y, load=expert_load(idx, E), ffn_count=ffn_count(idx, N),
                 offsets=offsets, perm_token=perm_token, slot_row=slot_row)
 

@@ -1,0 +1,100 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point, and rejects
+bad arguments on the host with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_router_amd as lm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "lc_moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lc_moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 8
+    lib = ctypes.CDLL(lm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(lm.EXPORTED)
+
+
+def test_status_and_stage_strings():
+    for s in range(7):
+        assert lm.status_str(s)
+    assert lm.status_str(99) == "unknown status"
+    assert [lm.stage_name(i) for i in range(lm.NUM_STAGES)] == ["route", "permute", "gate_up", "down", "combine"]
+    assert lm.stage_name(5) == "unknown"
+
+
+def good_shape():
+    return lm.make_shape(T=64, d=128, N=8, Z=4, K=2, I=256, dtype=lm.BF16)
+
+
+def test_workspace_size():
+    s = good_shape()
+    n = lm.lc_moe_workspace_size(s)
+    assert n > 0 and n % 256 == 0
+    # covers at least the FFN intermediates: T*K rows of I and of d bf16 values
+    assert n >= 64 * 2 * (256 + 128) * 2
+    bad = [dict(T=0), dict(K=13), dict(Z=-1), dict(d=100), dict(I=12), dict(dtype=7), dict(N=3000, Z=0, K=2),
+           dict(N=2048, Z=2049), dict(T=1 << 28, K=8)]
+    for kw in bad:
+        args = dict(T=64, d=128, N=8, Z=4, K=2, I=256, dtype=lm.BF16)
+        args.update(kw)
+        assert lm.lc_moe_workspace_size(lm.make_shape(**args)) == 0, kw
+    assert lm.lc_moe_workspace_size(lm.make_shape(T=64, d=132, N=8, Z=0, K=8, I=4, dtype=lm.F32)) > 0
+
+
+P = 1 << 20           # fake, 16-byte aligned device addresses: validation never dereferences
+MIS = P + 4           # misaligned
+
+
+def call_route(shape, x=P, wr=P, b=P, idx=P, gate=P, ws=P, nbytes=None):
+    nb = lm.lc_moe_workspace_size(good_shape()) if nbytes is None else nbytes
+    return lm._lib.lc_moe_route(ctypes.byref(shape) if shape is not None else None, x, wr, b, idx, gate,
+                                ws, nb, None)
+
+
+def test_route_validation():
+    s = good_shape()
+    assert call_route(None) == 1
+    assert call_route(s, x=None) == 1
+    assert call_route(s, gate=None) == 1
+    assert call_route(s, wr=MIS) == 4
+    assert call_route(s, ws=None) == 1
+    assert call_route(s, nbytes=100) == 5
+    assert call_route(lm.make_shape(64, 128, 8, 4, 2, 256, 5)) == 3
+    assert call_route(lm.make_shape(64, 128, 8, 4, 13, 256, lm.BF16)) == 2
+
+
+def test_expert_load_permute_forward_validation():
+    s = good_shape()
+    nb = lm.lc_moe_workspace_size(s)
+    L = lm._lib
+    sp = ctypes.byref(s)
+    assert L.lc_moe_expert_load(sp, None, P, None, P, nb, None) == 1
+    assert L.lc_moe_expert_load(sp, P, P, MIS, P, nb, None) == 4
+    assert L.lc_moe_expert_load(sp, P, P, None, P, nb - 1, None) == 5
+    assert L.lc_moe_permute(sp, P, P, None, P, P, None, None, P, nb, None) == 1
+    assert L.lc_moe_permute(sp, None, P, P, P, P, P, None, P, nb, None) == 1   # x needed for x_perm
+    assert L.lc_moe_permute(sp, P, P, P, P, MIS, None, None, P, nb, None) == 4
+    w = lm.Weights(P, P, P, P, P)
+    assert L.lc_moe_forward(sp, P, None, P, None, None, None, P, nb, None) == 1
+    assert L.lc_moe_forward(sp, P, ctypes.byref(w), None, None, None, None, P, nb, None) == 1
+    w2 = lm.Weights(P, P, MIS, P, P)
+    assert L.lc_moe_forward(sp, P, ctypes.byref(w2), P, None, None, None, P, nb, None) == 4
+    assert L.lc_moe_forward(sp, P, ctypes.byref(w), P, None, None, None, P, nb - 256, None) == 5
+    bad = lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)
+    bad.I = 6
+    assert L.lc_moe_forward(ctypes.byref(bad), P, ctypes.byref(w), P, None, None, None, P, nb, None) == 2
+    ev = (ctypes.c_void_p * 6)(*([P] * 5 + [0]))
+    assert L.lc_moe_forward_staged(sp, P, ctypes.byref(w), P, None, None, None, P, nb, None,
+                                   ctypes.cast(ev, ctypes.c_void_p)) == 1
