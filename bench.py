@@ -71,6 +71,9 @@ def run_steps(lm, st, steps, warmup):
     nst = lm.NUM_STAGES
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for row in evs:             # torch creates the hipEvent_t on the first record
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
