@@ -3,7 +3,7 @@
 Every step of the layer runs in the HIP library; this module converts torch tensors to
 device pointers and the current torch stream to a hipStream_t, checks tensor
 dtype/shape/device, and turns an error status into an exception.  torch is used only for
-device memory and streams.  Importing raises if the library has not been built
+device memory and streams.  The library is opened on first use and a missing build raises at once
 (``python -m mixture_experts_layer_router_amd.build``); there is no fallback path.
 
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
@@ -23,11 +23,6 @@ LIB_PATH = os.path.join(_PKG, "liblc_moe.so")
 # (libamdhip64.so.7).  Loaded in this order, liblc_moe.so binds to that runtime and the
 # process holds one HIP runtime; the other order would load two.
 import torch  # noqa: E402,F401
-
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m mixture_experts_layer_router_amd.build`")
-_lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
 NUM_STAGES = 5
@@ -61,9 +56,23 @@ _SIG = {
     "lc_moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lc_moe_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
-for _name, (_res, _args) in _SIG.items():
-    _f = getattr(_lib, _name)
-    _f.restype, _f.argtypes = _res, _args
+_LIB = None
+
+
+def lib():
+    """The loaded liblc_moe.so (opened on first use; raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mixture_experts_layer_router_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(handle, name)
+            f.restype, f.argtypes = res, args
+        _LIB = handle
+    return _LIB
+
 
 EXPORTED = tuple(_SIG)
 
@@ -72,7 +81,7 @@ class LcMoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {STATUS.get(status, status)} "
-                         f"({_lib.lc_moe_status_str(status).decode()})")
+                         f"({lib().lc_moe_status_str(status).decode()})")
 
 
 def _check(status: int, where: str):
@@ -81,11 +90,11 @@ def _check(status: int, where: str):
 
 
 def status_str(status: int) -> str:
-    return _lib.lc_moe_status_str(status).decode()
+    return lib().lc_moe_status_str(status).decode()
 
 
 def stage_name(i: int) -> str:
-    return _lib.lc_moe_stage_name(i).decode()
+    return lib().lc_moe_stage_name(i).decode()
 
 
 def make_shape(T, d, N, Z, K, I, dtype) -> Shape:
@@ -96,7 +105,7 @@ def make_shape(T, d, N, Z, K, I, dtype) -> Shape:
 
 
 def lc_moe_workspace_size(shape: Shape) -> int:
-    return int(_lib.lc_moe_workspace_size(ctypes.byref(shape)))
+    return int(lib().lc_moe_workspace_size(ctypes.byref(shape)))
 
 
 def _ptr(t):
@@ -117,20 +126,20 @@ def _nbytes(t):
 # ---- low-level: same names and argument order as the C-ABI ------------------------------
 
 def lc_moe_route(shape, x, w_router, bias, topk_idx, topk_gate, workspace, stream=None):
-    _check(_lib.lc_moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias),
+    _check(lib().lc_moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias),
                              _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace), _nbytes(workspace),
                              _stream(stream)), "lc_moe_route")
 
 
 def lc_moe_expert_load(shape, topk_idx, load, ffn_per_token, workspace, stream=None):
-    _check(_lib.lc_moe_expert_load(ctypes.byref(shape), _ptr(topk_idx), _ptr(load),
+    _check(lib().lc_moe_expert_load(ctypes.byref(shape), _ptr(topk_idx), _ptr(load),
                                    _ptr(ffn_per_token), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream)), "lc_moe_expert_load")
 
 
 def lc_moe_permute(shape, x, topk_idx, ffn_offsets, perm_token, slot_row, x_perm, load,
                    workspace, stream=None):
-    _check(_lib.lc_moe_permute(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(ffn_offsets),
+    _check(lib().lc_moe_permute(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(ffn_offsets),
                                _ptr(perm_token), _ptr(slot_row), _ptr(x_perm), _ptr(load),
                                _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "lc_moe_permute")
@@ -143,7 +152,7 @@ def _weights(w_router, bias, w_gate, w_up, w_down) -> Weights:
 
 def lc_moe_forward(shape, x, weights: Weights, y, topk_idx, topk_gate, load, workspace,
                    stream=None):
-    _check(_lib.lc_moe_forward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
+    _check(lib().lc_moe_forward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
                                _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _ptr(workspace),
                                _nbytes(workspace), _stream(stream)), "lc_moe_forward")
 
@@ -153,7 +162,7 @@ def lc_moe_forward_staged(shape, x, weights: Weights, y, topk_idx, topk_gate, lo
     arr = None
     if stage_events is not None:
         arr = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
-    _check(_lib.lc_moe_forward_staged(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
+    _check(lib().lc_moe_forward_staged(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream),
                                       ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None),

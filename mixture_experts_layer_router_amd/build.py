@@ -45,6 +45,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every kernel launched from host code must have its launch stub defined
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError(f"kernel launch stubs missing from {tmp}: {missing}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

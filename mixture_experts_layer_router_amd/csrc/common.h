@@ -19,8 +19,14 @@ constexpr int kMaxN = 2048;     // N limit (permutation bitmask LDS)
 constexpr int kTokBlock = 256;  // tokens per permutation block
 
 // M-tile height (rows of one expert) of the grouped FFN kernels.
-constexpr int kBmBf16 = 128;
+constexpr int kBmBf16 = 128;  // ffn_bf16_kernel (any d, I multiple of 8)
+constexpr int kBmPipe = 256;  // ffn_bf16_pipe_kernel (d and I multiples of 64)
 constexpr int kBmF32 = 64;
+
+// The pipelined bf16 FFN kernel needs whole 64-element K steps in both GEMMs.
+inline bool ffn_pipelined(const lc_moe_shape& s) {
+  return s.dtype == LC_MOE_BF16 && s.d % 64 == 0 && s.I % 64 == 0;
+}
 
 __device__ __forceinline__ float bf2f(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -55,7 +61,7 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   const size_t T = s.T, K = s.K, E = size_t(s.N) + s.Z, N = s.N;
   const size_t es = s.dtype == LC_MOE_BF16 ? 2 : 4;
   p.nblocks = int((T + kTokBlock - 1) / kTokBlock);
-  p.bm = s.dtype == LC_MOE_BF16 ? kBmBf16 : kBmF32;
+  p.bm = s.dtype == LC_MOE_BF16 ? (ffn_pipelined(s) ? kBmPipe : kBmBf16) : kBmF32;
   const size_t tk = T * K;
   size_t mt = N + (tk + p.bm - 1) / p.bm;
   if (mt > tk) mt = tk;

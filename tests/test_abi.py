@@ -20,7 +20,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert len(names) == 8
-    lib = ctypes.CDLL(lm.LIB_PATH)
+    lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lm.EXPORTED)
@@ -59,7 +59,7 @@ MIS = P + 4           # misaligned
 
 def call_route(shape, x=P, wr=P, b=P, idx=P, gate=P, ws=P, nbytes=None):
     nb = lm.lc_moe_workspace_size(good_shape()) if nbytes is None else nbytes
-    return lm._lib.lc_moe_route(ctypes.byref(shape) if shape is not None else None, x, wr, b, idx, gate,
+    return lm.lib().lc_moe_route(ctypes.byref(shape) if shape is not None else None, x, wr, b, idx, gate,
                                 ws, nb, None)
 
 
@@ -78,7 +78,7 @@ def test_route_validation():
 def test_expert_load_permute_forward_validation():
     s = good_shape()
     nb = lm.lc_moe_workspace_size(s)
-    L = lm._lib
+    L = lm.lib()
     sp = ctypes.byref(s)
     assert L.lc_moe_expert_load(sp, None, P, None, P, nb, None) == 1
     assert L.lc_moe_expert_load(sp, P, P, MIS, P, nb, None) == 4
