@@ -20,12 +20,12 @@ constexpr int kTokBlock = 256;  // tokens per permutation block
 
 // M-tile height (rows of one expert) of the grouped FFN kernels.
 constexpr int kBmBf16 = 128;  // ffn_bf16_kernel (any d, I multiple of 8)
-constexpr int kBmPipe = 256;  // ffn_bf16_pipe_kernel (d and I multiples of 64)
+constexpr int kBmPipe = 320;  // ffn_bf16_pipe_kernel (d and I multiples of 32)
 constexpr int kBmF32 = 64;
 
-// The pipelined bf16 FFN kernel needs whole 64-element K steps in both GEMMs.
+// The pipelined bf16 FFN kernel needs whole 32-element K steps in both GEMMs.
 inline bool ffn_pipelined(const lc_moe_shape& s) {
-  return s.dtype == LC_MOE_BF16 && s.d % 64 == 0 && s.I % 64 == 0;
+  return s.dtype == LC_MOE_BF16 && s.d % 32 == 0 && s.I % 32 == 0;
 }
 
 __device__ __forceinline__ float bf2f(bf16_t h) {
@@ -37,6 +37,15 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<bf16_t>(u >> 16);
+}
+
+// silu(g) * u for the bf16 FFN epilogues: silu(g) = g / (1 + e^-g) evaluated with the
+// hardware base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32; each within a few
+// ulp of fp32), far inside the bf16 rounding the result then takes.  Very negative g gives
+// e^-g = inf and a zero reciprocal, so silu -> -0; very positive g gives e^-g = 0 -> g.
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
 }
 
 // One M-tile of the grouped FFN: rows row0..row0+rows-1 of expert `expert`;

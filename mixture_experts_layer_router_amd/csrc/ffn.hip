@@ -177,8 +177,7 @@ __global__ __launch_bounds__(256, 2) void ffn_bf16_kernel(
           const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row < rows) {
             const float g = acc[i][nb][r], u = acc[i][nb + 2][r];
-            const float h = g / (1.f + expf(-g)) * u;
-            out[size_t(row0 + row) * ncols + col] = f2bf(h);
+            out[size_t(row0 + row) * ncols + col] = f2bf(swiglu_fast(g, u));
           }
         }
       }
@@ -200,33 +199,37 @@ __global__ __launch_bounds__(256, 2) void ffn_bf16_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Pipelined bf16 MFMA kernel (used when d and I are multiples of 32).
-// Tile: 256 rows x 256 weight rows, K step 32, 4-stage LDS ring (4 x 32 KB) filled by
-// direct global->LDS loads (global_load_lds_dwordx4), so up to three K steps are in
-// flight while one is multiplied.  256 threads = 2x2 waves; each wave owns 4x4 blocks of
-// 32x32 (v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane).  Wave row wm takes
-// the 32-row blocks 2*mb + wm, so a partly filled tile splits its blocks evenly.
-// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits in slot c ^ swz(r),
-// which spreads the 32 rows of one MFMA operand read over all banks.
+//
+// Tile: 320 rows x 256 weight rows, K step 32.  An expert with up to 320 rows is a single
+// tile, so its weights stream from HBM once (one M-tile per expert covers the prefill
+// layer, whose per-expert row counts cluster near T*K*(1-zero share)/N = 256).
+// 512 threads = 8 waves, two per SIMD.  Wave w owns the 32-row blocks 2*mb + (w >> 2)
+// (mb < 5) against two 32-column weight blocks chosen by w & 3: 5 x 2 blocks of 32x32
+// (v_mfma_f32_32x32x16_bf16), 160 fp32 accumulators per lane, which leaves room for two
+// full sets of operand fragments.  The waves sharing a SIMD (w, w + 4) take alternate row
+// blocks of the same columns, so a partly filled tile keeps every SIMD equally busy.
+//   MODE 0 (gate/up): weight rows 0..127 = gate rows n0..n0+127, 128..255 = up rows
+//                     n0..n0+127; a wave's two column blocks are the gate and up rows of
+//                     the same 32 outputs; activations gathered through perm_token;
+//                     epilogue silu(g)*u -> H (128 columns per tile).
+//   MODE 1 (down):    weight rows = W_down rows n0..n0+255; activations = H rows;
+//                     epilogue -> Y (256 columns per tile).
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4) through a
+// 4-stage ring (4 x 36 KB); activation row groups past the tile's rows are not loaded.
+// LDS row = 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits in slot c ^ swz(r).
+// Software pipeline: a K step has two substeps of 16 (one MFMA deep).  While one substep
+// multiplies, the wave reads all its fragments of the next substep into the other
+// register set.  Between the substeps of step kt each wave waits for its own LDS reads and
+// for its share of stage kt+1, then meets the others at a barrier; past it no wave reads
+// stage kt again, so the second substep refills stage kt's slot with stage kt+4, four
+// steps ahead of its use.
 // ---------------------------------------------------------------------------------------
-#ifndef LCM_PIPE_BK
-#define LCM_PIPE_BK 32
-#endif
 
-// XOR swizzle of the 16-byte chunk slot for LDS rows of CPR chunks (CPR = 4: 64-byte rows,
-// CPR = 8: 128-byte rows).  Conflict-free for the 32-row MFMA operand reads whether the
-// LDS serves 8 or 16 lanes of a ds_read_b128 per cycle.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  if (CPR == 4) return (((r >> 1) & 1) << 1) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
-  return (r & 7) ^ ((r >> 3) & 1);
+// XOR swizzle of the 16-byte chunk slot for 64-byte LDS rows: the 32 rows of one MFMA
+// operand read spread over all banks.
+__device__ __forceinline__ int swz4(int r) {
+  return (((r >> 1) & 1) << 1) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
 }
-
-#ifdef LCM_PROFILE
-__device__ unsigned long long lcm_prof[2][4096][6];
-extern "C" hipError_t lc_moe_debug_prof(void* host, size_t bytes) {
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(lcm_prof), bytes, 0, hipMemcpyDeviceToHost);
-}
-#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -238,39 +241,32 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define LCM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
 
+// Workgroup barrier without the vmcnt(0) that __syncthreads implies: the direct loads of
+// later stages stay in flight across it.
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Pipelined bf16 MFMA kernel (used when d and I are multiples of 32).
-// Tile: 256 rows x 256 weight rows, K step 32, 4-stage LDS ring (4 x 32 KB) filled by
-// direct global->LDS loads (global_load_lds_dwordx4): up to three K steps in flight.
-// 256 threads = 2x2 waves; wave (wm, wn) owns 4x4 blocks of 32x32 (v_mfma_f32_32x32x16_bf16,
-// 256 fp32 accumulators per lane): M blocks 2*mb + wm (a partly filled tile splits its
-// blocks evenly), N blocks = weight rows brow[nb].
-// Software pipeline: a K step has two substeps of 16.  The operand fragments of the next
-// substep are read from LDS while the MFMAs of the current one run; the barrier that
-// publishes the next stage sits between the two substeps, so every LDS read hides behind
-// 16 MFMAs.  The 8 loads of the stage three steps ahead are spread over the first
-// substep's MFMAs (one per two MFMAs) instead of bursting.
-// LDS row = 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits in slot c ^ swz(r).
-template <int MODE, int BK, int NST>
-__global__ __launch_bounds__(256, 1) void ffn_bf16_pipe_kernel(
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     const bf16_t* __restrict__ a_src, const int32_t* __restrict__ perm_token,
     const bf16_t* __restrict__ w0, const bf16_t* __restrict__ w1, bf16_t* __restrict__ out,
     const MTile* __restrict__ mtiles, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ n_mtiles_ptr, int kdim, int ncols, int n_ntiles) {
-  static_assert(BK == 32 && NST == 4, "stage body written for two 16-wide substeps");
-  constexpr int BM = kBmPipe;
-  constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
-  constexpr int RB = BK * 2;              // bytes per LDS row
-  constexpr int RPI = 64 / CPR;           // rows filled by one wave-wide DMA instruction
-  constexpr int IPW = 256 / (4 * RPI);    // DMA instructions per wave per operand per stage
+  constexpr int BM = kBmPipe;             // 320
+  constexpr int BK = 32, NST = 4;         // K step, ring stages
+  constexpr int LEAD = NST;               // stages loaded ahead of the one multiplied
+  constexpr int MB = BM / 64;             // row blocks per wave (5)
+  constexpr int RB = BK * 2;              // bytes per LDS row (64)
+  constexpr int RPI = 16;                 // rows filled by one wave-wide load
+  constexpr int NIA = BM / RPI;           // activation loads per stage (20)
+  constexpr int NIB = 256 / RPI;          // weight loads per stage (16)
+  constexpr int IA = (NIA + 7) / 8;       // activation load slots per wave (3)
+  constexpr int IB = NIB / 8;             // weight loads per wave (2)
   constexpr int A_BYTES = BM * RB;
-  constexpr int STAGE = A_BYTES + 256 * RB;
-  constexpr int VM_STAGE = 2 * IPW;       // loads per wave per stage
+  constexpr int STAGE = A_BYTES + 256 * RB;  // 36 KB
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
   int j, ntile;
@@ -280,18 +276,28 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_pipe_kernel(
   const int n0 = ntile * (MODE == 0 ? 128 : 256);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // DMA sources: wave w fills rows (IPW*w + i)*RPI .. +RPI of the A and B tiles;
-  // lane l writes LDS row l/CPR, slot l%CPR, i.e. global chunk (l%CPR) ^ swz(row).
-  const bf16_t* src[2 * IPW];
-  const int lrow = lane / CPR, lslot = lane % CPR;
+  // Load sources.  Activation load q (LDS rows 16q..16q+15) and weight load q belong to
+  // wave q % 8.  Lane l fills LDS row 16q + l/4, slot l%4, with global chunk
+  // (l%4) ^ swz4(row).  Activation loads whose 16 rows all lie past the tile's rows are
+  // skipped; they are a suffix of the wave's list, so the wave issues its first na.
+  const bf16_t* srcA[IA];
+  const bf16_t* srcB[IB];
+  const int lrow = lane >> 2, lslot = lane & 3;
+  int na = 0;
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * RPI + lrow;
-    const int chunk = (lslot ^ swz<CPR>(r)) * 8;
+  for (int i = 0; i < IA; ++i) {
+    const int q = wave + 8 * i;
+    const int r = q * RPI + lrow;
+    na += (q < NIA && q * RPI < rows) ? 1 : 0;
     const int ar = r < rows ? r : 0;  // rows past the tile read a valid row; never stored
     const size_t src_row = MODE == 0 ? size_t(perm_token[row0 + ar]) : size_t(row0 + ar);
-    src[i] = a_src + src_row * kdim + chunk;
+    srcA[i] = a_src + src_row * kdim + (lslot ^ swz4(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int r = (wave + 8 * i) * RPI + lrow;  // weight row of the tile, 0..255
     int c;
     const bf16_t* mat;
     if (MODE == 0) {
@@ -301,160 +307,137 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_pipe_kernel(
       c = n0 + r;
       mat = w0;
     }
-    const int brow = c < ncols ? c : n0;
-    src[IPW + i] = mat + (size_t(e) * ncols + brow) * kdim + chunk;
+    const int brow = c < ncols ? c : n0;  // columns past the matrix repeat a valid row
+    srcB[i] = mat + (size_t(e) * ncols + brow) * kdim + (lslot ^ swz4(r)) * 8;
   }
+  const int per_stage = na + IB;  // this wave's loads per stage (vmcnt increments)
   const int nk = kdim / BK;
 #ifdef LCM_NO_KROT
   const int krot = 0;
 #else
   // Each work unit starts its K loop at its own offset: rows of one tile share their low
   // address bits (row strides are multiples of 4 KB), so tiles running side by side are
-  // spread over the L2 channels.
+  // spread over the memory channels.
   const int krot = (j * 7 + ntile * 3) % nk;
 #endif
   auto kphys = [&](int kt) { const int k = kt + krot; return (k >= nk ? k - nk : k) * BK; };
-  auto issue_one = [&](int i, unsigned char* st, int k0) {
-    dma16(src[i] + k0, st + (i < IPW ? 0 : A_BYTES) + (wave * IPW + (i % IPW)) * 1024);
+  // this wave's load number i (0..IA+IB-1) of stage kt
+  auto issue_one = [&](int i, int kt) {
+    unsigned char* st = smem + (kt % NST) * STAGE;
+    if (i < IA) {
+      if (i < na) dma16(srcA[i] + kphys(kt), st + (wave + 8 * i) * 1024);
+    } else {
+      dma16(srcB[i - IA] + kphys(kt), st + A_BYTES + (wave + 8 * (i - IA)) * 1024);
+    }
   };
+  // s_waitcnt vmcnt(n) for a run-time n (0..(LEAD-1)*(IA+IB))
+  auto wait_vm = [&](int n) {
+    switch (n) {
+#define LCM_CASE(k) case k: LCM_WAIT_VMCNT(k); break;
+      LCM_CASE(0) LCM_CASE(1) LCM_CASE(2) LCM_CASE(3) LCM_CASE(4) LCM_CASE(5) LCM_CASE(6)
+      LCM_CASE(7) LCM_CASE(8) LCM_CASE(9) LCM_CASE(10) LCM_CASE(11) LCM_CASE(12) LCM_CASE(13)
+      LCM_CASE(14)
+#undef LCM_CASE
+      default: LCM_WAIT_VMCNT(15); break;
+    }
+  };
+  // wait until this wave's loads of stage s landed, `newest` being the last stage issued
+  auto wait_stage = [&](int s, int newest) { wait_vm((newest - s) * per_stage); };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, sw = swz<CPR>(l32), khalf = lane >> 5;
-  int brow[4];
+  const int l32 = lane & 31, sw = swz4(l32), khalf = lane >> 5;
+  int boff[2];  // LDS byte offset of this lane's row in the wave's two weight blocks
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    brow[nb] = MODE == 0 ? (nb >> 1) * 128 + wn * 64 + (nb & 1) * 32 : wn * 128 + nb * 32;
-  bool bv[4];
+  for (int nb = 0; nb < 2; ++nb)
+    boff[nb] = A_BYTES + ((MODE == 0 ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + l32) * RB;
+  int nvb = 0;  // row blocks of this wave holding tile rows (a prefix in mb)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) bv[mb] = (mb * 2 + wm) * 32 < rows;
+  for (int mb = 0; mb < MB; ++mb) nvb += (mb * 2 + wm) * 32 < rows;
 
-  f32x16 acc[4][4];
+  f32x16 acc[MB][2];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
 
-  for (int s = 0; s < NST - 1 && s < nk; ++s) {
-#pragma unroll
-    for (int i = 0; i < 2 * IPW; ++i) issue_one(i, smem + s * STAGE, kphys(s));
-  }
-  // wait until stage kt landed, with `ahead` later stages allowed in flight
-  auto wait_stage = [&](int ahead) {
-    if (ahead >= 2) LCM_WAIT_VMCNT(2 * VM_STAGE);
-    else if (ahead == 1) LCM_WAIT_VMCNT(VM_STAGE);
-    else LCM_WAIT_VMCNT(0);
-  };
+  const int npro = nk < LEAD ? nk : LEAD;
+  for (int s = 0; s < npro; ++s)
+    for (int i = 0; i < IA + IB; ++i) issue_one(i, s);
 
-  auto run = [&](auto full) {
-    constexpr bool FULL = decltype(full)::value;
-    auto read = [&](const unsigned char* st, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+  auto run = [&](auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;  // row blocks holding tile rows
+    auto rd = [&](int kt, int ks, bf16x8 (&a)[MB], bf16x8 (&b)[2]) {
+      const unsigned char* st = smem + (kt % NST) * STAGE;
       const int slot = ((ks * 2 + khalf) ^ sw) * 16;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        fb[nb] = *reinterpret_cast<const bf16x8*>(st + A_BYTES + (brow[nb] + l32) * RB + slot);
+      for (int mb = 0; mb < NV; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(st + ((mb * 2 + wm) * 32 + l32) * RB + slot);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        if (FULL || bv[mb])
-          fa[mb] = *reinterpret_cast<const bf16x8*>(st + ((mb * 2 + wm) * 32 + l32) * RB + slot);
+      for (int nb = 0; nb < 2; ++nb) b[nb] = *reinterpret_cast<const bf16x8*>(st + boff[nb] + slot);
     };
-    // 16 MFMAs of one substep.  DMA: the wave's 8 loads of the stage NST-1 ahead go between
-    // them; `after_first` runs after the first MFMA pair (used to start the next substep's
-    // LDS reads once this substep's operands are known to be in registers).
-    auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], auto dma, unsigned char* nst,
-                     int k0n, auto after_first) {
+    // MFMAs of one substep; with DMA, this wave's loads of stage kt_load go one per row
+    // block, the rest after the last block.
+    auto mm = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[2], auto dma, int kt_load) {
       constexpr bool DMA = decltype(dma)::value;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < NV; ++mb) {
+        if (DMA && mb < IA + IB) issue_one(mb, kt_load);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (DMA) issue_one(mb * 2 + h, nst, k0n);
-          __builtin_amdgcn_sched_barrier(0);
-          if (FULL || bv[mb]) {
-#pragma unroll
-            for (int nb = h * 2; nb < h * 2 + 2; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          if (mb == 0 && h == 0) after_first();
-        }
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
       }
+      if (DMA)
+        for (int i = NV; i < IA + IB; ++i) issue_one(i, kt_load);
     };
-#ifdef LCM_PROFILE
-    unsigned long long pt[6] = {0, 0, 0, 0, 0, 0};
-    const unsigned long long tstart = __builtin_amdgcn_s_memtime();
-#endif
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
-    wait_stage(nk - 1 < NST - 2 ? nk - 1 : NST - 2);
+    bf16x8 ca[MB], cb[2], xa[MB], xb[2];  // fragments of the current / next substep
+    wait_stage(0, npro - 1);
     block_barrier();
-    read(smem, 0, a0, b0);
+    rd(0, 0, ca, cb);
     auto step = [&](int kt, auto more_tag, auto last_tag) {
-      constexpr bool MORE = decltype(more_tag)::value;
       constexpr bool LAST = decltype(last_tag)::value;
-      const unsigned char* st = smem + (kt % NST) * STAGE;
-      mfmas(a0, b0, more_tag, smem + ((kt + NST - 1) % NST) * STAGE, kphys(kt + NST - 1),
-            [&] { read(st, 1, a1, b1); });
+      rd(kt, 1, xa, xb);
+      mm(ca, cb, std::false_type{}, 0);
       if (!LAST) {
-#ifdef LCM_PROFILE
-        unsigned long long t0 = __builtin_amdgcn_s_memtime();
-#endif
-        // stage kt+1 must have landed; stages after it may stay in flight
-        const int issued_after = (MORE ? kt + NST - 1 : nk - 1) - (kt + 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt done
-        wait_stage(issued_after);
-#ifdef LCM_PROFILE
-        unsigned long long t1 = __builtin_amdgcn_s_memtime();
-        pt[0] += t1 - t0;
-#endif
-        block_barrier();
-#ifdef LCM_PROFILE
-        pt[1] += __builtin_amdgcn_s_memtime() - t1;
-#endif
-        read(smem + ((kt + 1) % NST) * STAGE, 0, a0, b0);
+        const int newest = kt + LEAD - 1 < nk - 1 ? kt + LEAD - 1 : nk - 1;
+        wait_stage(kt + 1, newest);
+        block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again
+        rd(kt + 1, 0, ca, cb);
       }
-      mfmas(a1, b1, std::false_type{}, nullptr, 0, [] {});
+      mm(xa, xb, more_tag, kt + LEAD);
     };
-    // main steps load the stage NST-1 ahead; the last NST-1 steps have nothing left to load;
-    // the final step has no next stage to publish
-    const int nmain = nk - (NST - 1) > 0 ? nk - (NST - 1) : 0;
+    const int nmain = nk - LEAD > 0 ? nk - LEAD : 0;
     for (int kt = 0; kt < nmain; ++kt) step(kt, std::true_type{}, std::false_type{});
     for (int kt = nmain; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
     step(nk - 1, std::false_type{}, std::true_type{});
-#ifdef LCM_PROFILE
-    unsigned long long tend = __builtin_amdgcn_s_memtime();
-    pt[4] = tend - tstart;
-    pt[3] = pt[4] - pt[0] - pt[1];
-    pt[5] = FULL ? 1 : 0;
-    if (lane == 0 && blockIdx.x < 4096 * 8 && (blockIdx.x & 7) == 0 && wave == 0)
-      for (int q = 0; q < 6; ++q) lcm_prof[MODE][blockIdx.x >> 3][q] = pt[q];
-#endif
   };
-  if (bv[3]) run(std::true_type{});
-  else run(std::false_type{});
+  switch (nvb) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    default: run(std::integral_constant<int, 5>{}); break;
+  }
 
   // epilogue; 32x32 D layout: column lane & 31, rows 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    if (!bv[mb]) continue;
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nvb) continue;
     if (MODE == 0) {
+      const int col = n0 + wn * 32 + l32;
+      if (col >= ncols) continue;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n0 + wn * 64 + nb * 32 + l32;
-        if (col >= ncols) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (mb * 2 + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-          if (row < rows) {
-            const float g = acc[mb][nb][r], u = acc[mb][nb + 2][r];
-            out[size_t(row0 + row) * ncols + col] = f2bf(g / (1.f + expf(-g)) * u);
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = (mb * 2 + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < rows)
+          out[size_t(row0 + row) * ncols + col] = f2bf(swiglu_fast(acc[mb][0][r], acc[mb][1][r]));
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = n0 + wn * 128 + nb * 32 + l32;
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = n0 + wn * 64 + nb * 32 + l32;
         if (col >= ncols) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -466,14 +449,11 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_pipe_kernel(
   }
 }
 
-constexpr int kPipeBK = LCM_PIPE_BK;
-constexpr int kPipeNST = (160 * 1024) / (2 * 256 * LCM_PIPE_BK * 2) < 4 ? (160 * 1024) / (2 * 256 * LCM_PIPE_BK * 2) : 4;
-
-template __global__ void ffn_bf16_pipe_kernel<0, kPipeBK, kPipeNST>(
+template __global__ void ffn_bf16_pipe_kernel<0>(
     const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,
     const bf16_t* __restrict__, bf16_t* __restrict__, const MTile* __restrict__,
     const int32_t* __restrict__, const int32_t* __restrict__, int, int, int);
-template __global__ void ffn_bf16_pipe_kernel<1, kPipeBK, kPipeNST>(
+template __global__ void ffn_bf16_pipe_kernel<1>(
     const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,
     const bf16_t* __restrict__, bf16_t* __restrict__, const MTile* __restrict__,
     const int32_t* __restrict__, const int32_t* __restrict__, int, int, int);
@@ -547,7 +527,7 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
     const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
-    ffn_bf16_pipe_kernel<0, kPipeBK, kPipeNST><<<dim3(grid), dim3(256), 0, st>>>(
+    ffn_bf16_pipe_kernel<0><<<dim3(grid), dim3(512), 0, st>>>(
         static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
         static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
         s.I, nn);
@@ -578,7 +558,7 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
     const int nn = (s.d + 255) / 256;
     const size_t units = size_t(mt_max) * nn;
     const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
-    ffn_bf16_pipe_kernel<1, kPipeBK, kPipeNST><<<dim3(grid), dim3(256), 0, st>>>(
+    ffn_bf16_pipe_kernel<1><<<dim3(grid), dim3(512), 0, st>>>(
         static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
         static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn);
   } else if (s.dtype == LC_MOE_BF16) {
