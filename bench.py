@@ -8,9 +8,15 @@ workload's resident inputs.  Prints ONE JSON line.  value = tokens/s of the whol
 (inputs and weights already in HBM).  Per-stage times come from HIP events recorded by
 lc_moe_forward_staged on the launch stream inside the timed region.
 
-roofline: the dominant kernel is the gate/up grouped GEMM (two thirds of the FFN FLOPs
-and weight bytes); achieved = its algorithmic FLOPs per launch (4*d*I per FFN pick) over
-its mean event-timed duration, against the dense bf16 MFMA peak.
+roofline: the dominant kernel is the gate/up grouped GEMM (ffn_bf16_pipe_kernel<0>: two
+thirds of the FFN FLOPs and weight bytes).  At this shape its HBM floor (algorithmic bytes
+/ 8 TB/s) lies above its MFMA floor (FLOPs / 2.5 PFLOP/s), so the bound is HBM: achieved =
+algorithmic bytes per launch (gate and up weights of every touched expert, 2*I*d*2 bytes
+each, plus d*2 bytes of x read and I*2 bytes of H written per FFN pick) over the mean
+event-timed launch duration.  The MFMA fraction (4*d*I FLOPs per FFN pick) is reported
+beside it.  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+(scaled by a plain-copy calibration), read from the committed profile summary and dropped
+(null) when the kernel source no longer matches the one the counters were taken on.
 decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
 (gate/up + down) is bound by streaming the weights of the experts that received at least
 one token; reported against the HBM peak.
@@ -31,11 +37,40 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_gate_up_prefill_T16384_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_router_amd", "csrc", f)
+                  for f in ("ffn.hip", "common.h")]
 METRIC = "MoE-layer tokens/s and % of bf16 MFMA peak (prefill) / % HBM peak (decode)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None when the
+    summary is for another workload or another version of the kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def setup(wl, dev):
@@ -193,6 +228,8 @@ def main():
     st_ms = {k: float(np.mean(v)) for k, v in stages.items()}
     gu_flops = 4.0 * wl.d * wl.I * nnz
     dn_flops = 2.0 * wl.d * wl.I * nnz
+    gu_bytes = touched * 2.0 * wl.I * wl.d * 2 + nnz * (wl.d + wl.I) * 2.0
+    gu_gbs = gu_bytes / (st_ms["gate_up"] * 1e-3) / 1e9
     gu_tflops = gu_flops / (st_ms["gate_up"] * 1e-3) / 1e12
     ffn_ms = st_ms["gate_up"] + st_ms["down"]
     ffn_tflops = (gu_flops + dn_flops) / (ffn_ms * 1e-3) / 1e12
@@ -216,10 +253,14 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": wl.description, "T": wl.T, "d": wl.d, "N": wl.N, "Z": wl.Z,
                    "K": wl.K, "I": wl.I, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "ffn_bf16_kernel<0> (gate/up + SwiGLU)",
-                     "achieved": gu_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                     "flops_per_launch": gu_flops, "launch_ms": st_ms["gate_up"]},
+        "roofline": {"bound": "hbm", "kernel": "lcm::ffn_bf16_pipe_kernel<0> (gate/up + SwiGLU)",
+                     "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "algorithmic_bytes": gu_bytes, "flops_per_launch": gu_flops,
+                     "mfma_tflops": gu_tflops, "mfma_frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "hbm_floor_ms": gu_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+                     "mfma_floor_ms": gu_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3,
+                     "launch_ms": st_ms["gate_up"]},
         "ffn": {"rows": nnz, "touched_experts": touched, "ms": ffn_ms, "TFLOPs": ffn_tflops,
                 "mfma_frac": ffn_tflops / MFMA_BF16_PEAK_TFLOPS,
                 "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
