@@ -148,6 +148,39 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* stage_events);
 
+/* PID gains of the expert-bias controller (host struct). */
+typedef struct {
+  float kp, ki, kd;
+} lc_moe_pid;
+
+/* Expert-bias controller: one update of the selection bias from the last step's loads.
+ * The pages say only that the bias follows recent expert usage and that its update rule
+ * is a PID controller adjusting it in real time, which keeps the activated parameters
+ * per token within a band (LongCat-Flash article, section "Zero-computation experts",
+ * bias paragraph).  Error signal and gains are not given; this library takes, for every
+ * expert i of the pool (FFN and zero-computation alike), in fp32:
+ *   e_i        = target_i - load_i / (T*K)           (load_i and T*K converted to fp32,
+ *                                                     IEEE division)
+ *   integral_i = integral_i + e_i
+ *   bias_i     = bias_i + (kp*e_i + ki*integral_i + kd*(e_i - prev_err_i))
+ *   prev_err_i = e_i
+ * so an expert picked less often than its target share gains bias.  Targets on the
+ * zero-computation experts set the zero share of the picks, hence the mean number of FFN
+ * experts per token.
+ *   gains      host struct {kp, ki, kd}
+ *   load       [N+Z] int32            picks per expert (lc_moe_expert_load / lc_moe_forward)
+ *   target     [N+Z] fp32             target share of the T*K picks per expert (the
+ *                                     caller's choice; normally summing to 1)
+ *   bias       [N+Z] fp32 (in/out)
+ *   integral   [N+Z] fp32 (in/out)    running sum of the errors; zero before the first call
+ *   prev_err   [N+Z] fp32 (in/out)    previous error; zero before the first call, so the
+ *                                     first derivative term is kd*e_i
+ * Reads T, K, N, Z of shape (which must pass the usual checks).  bias, integral and
+ * prev_err may not alias each other or load/target. */
+lc_moe_status lc_moe_bias_update(const lc_moe_shape* shape, const lc_moe_pid* gains,
+                                 const int32_t* load, const float* target, float* bias,
+                                 float* integral, float* prev_err, hipStream_t stream);
+
 /* Static strings; never NULL. */
 const char* lc_moe_status_str(lc_moe_status status);
 const char* lc_moe_stage_name(int stage);

@@ -7,9 +7,9 @@ device memory and streams.  The library is opened on first use and a missing bui
 (``python -m mixture_experts_layer_router_amd.build``); there is no fallback path.
 
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
-``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``,
-``lc_moe_workspace_size``); ``route``, ``expert_load``, ``permute`` and ``forward``
-allocate the outputs and a workspace with torch and call them.
+``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_bias_update``,
+``lc_moe_workspace_size``); ``route``, ``expert_load``, ``permute``, ``forward`` and
+``bias_update`` allocate outputs and a workspace with torch where needed and call them.
 """
 from __future__ import annotations
 
@@ -42,6 +42,10 @@ class Weights(ctypes.Structure):
                 ("w_down", ctypes.c_void_p)]
 
 
+class Pid(ctypes.Structure):
+    _fields_ = [("kp", ctypes.c_float), ("ki", ctypes.c_float), ("kd", ctypes.c_float)]
+
+
 _vp, _sz = ctypes.c_void_p, ctypes.c_size_t
 _SIG = {
     "lc_moe_workspace_size": (_sz, [ctypes.POINTER(Shape)]),
@@ -53,6 +57,8 @@ _SIG = {
                                       _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_forward_staged": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights),
                                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "lc_moe_bias_update": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Pid), _vp, _vp,
+                                          _vp, _vp, _vp, _vp]),
     "lc_moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lc_moe_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -169,6 +175,12 @@ def lc_moe_forward_staged(shape, x, weights: Weights, y, topk_idx, topk_gate, lo
            "lc_moe_forward_staged")
 
 
+def lc_moe_bias_update(shape, gains: Pid, load, target, bias, integral, prev_err, stream=None):
+    _check(lib().lc_moe_bias_update(ctypes.byref(shape), ctypes.byref(gains), _ptr(load),
+                                   _ptr(target), _ptr(bias), _ptr(integral), _ptr(prev_err),
+                                   _stream(stream)), "lc_moe_bias_update")
+
+
 # ---- convenience wrappers: allocate outputs with torch, then call the C entry point -----
 
 def _shape_of(x, N, Z, K, I):
@@ -243,3 +255,11 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_ev
     else:
         lc_moe_forward_staged(shape, x, wts, y, idx, gate, load, ws, stage_events=stage_events)
     return dict(y=y, topk_idx=idx, topk_gate=gate, load=load)
+
+
+def bias_update(load, target, bias, integral, prev_err, T, K, N, kp, ki, kd):
+    """One PID update of bias, integral and prev_err (all fp32 [E], updated in place) from
+    the int32 [E] loads of a step of T tokens with K picks each."""
+    E = load.shape[0]
+    shape = make_shape(T, 8, N, E - N, K, 8, BF16)
+    lc_moe_bias_update(shape, Pid(kp, ki, kd), load, target, bias, integral, prev_err)

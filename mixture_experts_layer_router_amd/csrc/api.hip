@@ -199,6 +199,23 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   return LC_MOE_OK;
 }
 
+lc_moe_status lc_moe_bias_update(const lc_moe_shape* shape, const lc_moe_pid* gains,
+                                 const int32_t* load, const float* target, float* bias,
+                                 float* integral, float* prev_err, hipStream_t stream) {
+  LCM_CHECK(check_shape(shape));
+  if (!gains) return LC_MOE_E_NULLPTR;
+  LCM_CHECK(check_ptr(load));
+  LCM_CHECK(check_ptr(target));
+  LCM_CHECK(check_ptr(bias));
+  LCM_CHECK(check_ptr(integral));
+  LCM_CHECK(check_ptr(prev_err));
+  const int E = shape->N + shape->Z;
+  LCM_LAUNCH(launch_bias_update(E, static_cast<long long>(shape->T) * shape->K, gains->kp,
+                                gains->ki, gains->kd, load, target, bias, integral, prev_err,
+                                stream));
+  return LC_MOE_OK;
+}
+
 lc_moe_status lc_moe_forward(const lc_moe_shape* shape, const void* x,
                              const lc_moe_weights* weights, void* y, int32_t* topk_idx,
                              float* topk_gate, int32_t* load, void* workspace,

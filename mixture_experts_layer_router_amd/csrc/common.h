@@ -133,4 +133,9 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
 hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,
                           const int32_t* slot_row, const float* gate, void* y, hipStream_t st);
 
+// One PID update of the selection bias over the E = N+Z experts.
+hipError_t launch_bias_update(int E, long long tk, float kp, float ki, float kd,
+                              const int32_t* load, const float* target, float* bias,
+                              float* integral, float* prev_err, hipStream_t st);
+
 }  // namespace lcm

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -98,3 +98,16 @@ def test_expert_load_permute_forward_validation():
     ev = (ctypes.c_void_p * 6)(*([P] * 5 + [0]))
     assert L.lc_moe_forward_staged(sp, P, ctypes.byref(w), P, None, None, None, P, nb, None,
                                    ctypes.cast(ev, ctypes.c_void_p)) == 1
+
+
+def test_bias_update_validation():
+    s = good_shape()
+    g = lm.Pid(0.5, 0.05, 0.0)
+    f = lm.lib().lc_moe_bias_update
+    assert f(None, ctypes.byref(g), P, P, P, P, P, None) == 1
+    assert f(ctypes.byref(s), None, P, P, P, P, P, None) == 1
+    assert f(ctypes.byref(s), ctypes.byref(g), None, P, P, P, P, None) == 1
+    assert f(ctypes.byref(s), ctypes.byref(g), P, P, P, P, None, None) == 1
+    assert f(ctypes.byref(s), ctypes.byref(g), P, MIS, P, P, P, None) == 4
+    assert f(ctypes.byref(lm.make_shape(64, 128, 8, 4, 13, 256, lm.BF16)), ctypes.byref(g), P, P, P, P, P,
+             None) == 2
