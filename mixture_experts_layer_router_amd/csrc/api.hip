@@ -101,7 +101,8 @@ lc_moe_status lc_moe_route(const lc_moe_shape* shape, const void* x, const float
   WsPlan p;
   LCM_CHECK(check_ws(shape, workspace, workspace_bytes, p));
   float* logits = at<float>(workspace, p.logits);
-  LCM_LAUNCH(launch_router_logits(*shape, x, w_router, logits, stream));
+  LCM_LAUNCH(launch_router_logits(*shape, x, w_router, at<bf16_t>(workspace, p.wsplit), logits,
+                                  at<float>(workspace, p.rpart), stream));
   LCM_LAUNCH(launch_router_topk(*shape, logits, bias, topk_idx, topk_gate, stream));
   return LC_MOE_OK;
 }
@@ -183,7 +184,9 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   void* ybuf = at<char>(workspace, p.ybuf);
 
   if (!mark(0)) return LC_MOE_E_DEVICE;
-  LCM_LAUNCH(launch_router_logits(s, x, weights->w_router, at<float>(workspace, p.logits), stream));
+  LCM_LAUNCH(launch_router_logits(s, x, weights->w_router, at<bf16_t>(workspace, p.wsplit),
+                                  at<float>(workspace, p.logits), at<float>(workspace, p.rpart),
+                                  stream));
   LCM_LAUNCH(launch_router_topk(s, at<float>(workspace, p.logits), weights->bias, idx, gate, stream));
   if (!mark(1)) return LC_MOE_E_DEVICE;
   LCM_CHECK(permute_core(s, idx, p, workspace, ld, offsets, slot_row, perm_token, nullptr, stream));

@@ -54,10 +54,30 @@ struct MTile {
   int expert, row0, rows, first_tile;
 };
 
+// Split-K of the bf16 router GEMM.  Its tiles are 128 tokens x 128 experts; when the
+// layer has few tokens (decode) there are too few tiles to fill 256 CUs, so the reduction
+// over d is cut into `splits` chunks of `chunk` columns (a multiple of 32) whose partial
+// logits are summed, in chunk order, by a reduction kernel.
+struct RouterSplit {
+  int splits, chunk;
+};
+inline RouterSplit router_split(const lc_moe_shape& s) {
+  RouterSplit r{1, s.d};
+  if (s.dtype != LC_MOE_BF16) return r;
+  const long long tiles = (long long)((s.N + s.Z + 127) / 128) * ((s.T + 127) / 128);
+  long long want = (512 + tiles - 1) / tiles;
+  const int kmax = (s.d + 31) / 32;
+  if (want > kmax) want = kmax;
+  if (want <= 1) return r;
+  r.chunk = ((s.d + int(want) - 1) / int(want) + 31) / 32 * 32;
+  r.splits = (s.d + r.chunk - 1) / r.chunk;
+  return r;
+}
+
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsPlan {
-  size_t logits, idx, gate, block_counts, block_base, load, offsets, mtiles, n_mtiles,
-      perm_token, slot_row, hbuf, ybuf, total;
+  size_t logits, wsplit, rpart, idx, gate, block_counts, block_base, load, offsets, mtiles,
+      n_mtiles, perm_token, slot_row, hbuf, ybuf, total;
   int nblocks;  // token blocks of the permutation
   int bm;       // M-tile height for this dtype
   int mt_max;   // capacity of the M-tile list
@@ -78,6 +98,10 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   p.logits = take(T * E * 4);
+  const RouterSplit rs = router_split(s);
+  // the fp32 router weight as three bf16 parts (bf16 layers)
+  p.wsplit = take(s.dtype == LC_MOE_BF16 ? 3 * E * size_t(s.d) * 2 : 0);
+  p.rpart = take(rs.splits > 1 ? size_t(rs.splits) * T * E * 4 : 0);
   p.idx = take(tk * 4);
   p.gate = take(tk * 4);
   p.block_counts = take(size_t(p.nblocks) * E * 4);
@@ -96,9 +120,12 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
 
 // ---- launchers (host functions defined in the .hip files) ------------------------------
 
-// Router logits L[T][E] = x W_r^T (fp32 result).
+// Router logits L[T][E] = x W_r^T (fp32 result).  bf16 layers: W_r is first split into
+// three bf16 parts (wsplit, 3*E*d bf16); with more than one split (router_split) the
+// GEMM writes `splits` partial logit arrays [splits][T][E] to rpart, which are then summed
+// in split order into logits.
 hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
-                                float* logits, hipStream_t st);
+                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st);
 // Softmax over E, biased top-K; writes idx [T][K] and gate [T][K].
 hipError_t launch_router_topk(const lc_moe_shape& s, const float* logits, const float* bias,
                               int32_t* idx, float* gate, hipStream_t st);

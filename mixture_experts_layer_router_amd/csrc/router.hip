@@ -6,7 +6,9 @@
 //   bf16 x: bf16 MFMA.  Each fp32 router weight is split exactly into three bf16 parts
 //   w = hi + mid + lo (8 significant bits each; the remainders are exact in fp32), every
 //   product of a bf16 x with a part is exact in fp32, and the MFMA sums them in fp32 --
-//   an fp32 dot product at bf16-MFMA rate (3 MFMAs per fp32 product).
+//   an fp32 dot product at bf16-MFMA rate (3 MFMAs per fp32 product).  With few tokens
+//   the reduction is split over workgroups and the partial sums are added in split
+//   order by a reduction kernel (no atomics).
 //   fp32 x: plain fp32 FMA, LDS-tiled.
 // Stage 2 (top-K): one wavefront per token: max, exp, sum and divide in fp32, then K
 //   rounds of a wavefront argmax over s = p + b (ties -> lower index) by shuffles.
@@ -15,8 +17,11 @@
 namespace lcm {
 
 // ---------------------------------------------------------------------------------------
-// bf16 MFMA logits.  Tile: 128 tokens x 128 experts, K step 32, 256 threads (2x2 waves,
-// 64x64 per wave, v_mfma_f32_32x32x16_bf16).
+// bf16 MFMA logits.  W_r is split once per call into three bf16 matrices (hi, mid, lo);
+// the GEMM then reads bf16 operands only.  Tile: 128 tokens x 128 experts, K step 32,
+// 256 threads (2x2 waves, 64x64 per wave, v_mfma_f32_32x32x16_bf16, three MFMAs per
+// block and k step, one per part).  blockIdx.z picks a chunk of the reduction (split-K
+// for layers with few tokens); each chunk's partial logits go to their own array.
 // ---------------------------------------------------------------------------------------
 namespace rl {
 constexpr int BM = 128, BN = 128, BK = 32, LDA = BK + 8;  // LDS row: 80 bytes
@@ -30,9 +35,25 @@ __device__ __forceinline__ void split3(float w, bf16_t& hi, bf16_t& mid, bf16_t&
   lo = f2bf(r2);
 }
 
+// wsplit = [hi | mid | lo], each [E][d] bf16: n = E*d fp32 weights, 4 per thread.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
+                                                           bf16_t* __restrict__ wsplit, size_t n) {
+  const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float4 w = *reinterpret_cast<const float4*>(wr + i);
+  bf16_t h[4], m[4], l[4];
+  split3(w.x, h[0], m[0], l[0]);
+  split3(w.y, h[1], m[1], l[1]);
+  split3(w.z, h[2], m[2], l[2]);
+  split3(w.w, h[3], m[3], l[3]);
+  *reinterpret_cast<uint2*>(wsplit + i) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+  *reinterpret_cast<uint2*>(wsplit + n + i) = make_uint2(m[0] | (uint32_t(m[1]) << 16), m[2] | (uint32_t(m[3]) << 16));
+  *reinterpret_cast<uint2*>(wsplit + 2 * n + i) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+}
+
 __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
-    const bf16_t* __restrict__ x, const float* __restrict__ wr, float* __restrict__ logits,
-    int T, int d, int E) {
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, float* __restrict__ out,
+    int T, int d, int E, int chunk) {
   using namespace rl;
   __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDA];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[3][BN * LDA];
@@ -40,64 +61,45 @@ __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
   const int tid = threadIdx.x;
   const int e0 = blockIdx.x * BN;
   const int t0 = blockIdx.y * BM;
+  const int kbeg = blockIdx.z * chunk;
+  const int kend = kbeg + chunk < d ? kbeg + chunk : d;
+  float* logits = out + size_t(blockIdx.z) * T * E;
+  const size_t part = size_t(E) * d;
 
-  // global -> register prefetch assignment
-  // A: 128 rows x 4 chunks of 8 bf16 -> 2 chunks per thread
+  // global -> register prefetch: 128 rows x 4 chunks of 8 bf16 per operand -> 2 per thread
   const bf16_t* a_ptr[2];
-  int a_kc[2], a_row[2];
+  const bf16_t* b_ptr[2];
+  int r_row[2], r_kc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    int c = tid + i * 256;
-    a_row[i] = c >> 2;
-    a_kc[i] = (c & 3) * 8;
-    int t = t0 + a_row[i];
+    const int c = tid + i * 256;
+    r_row[i] = c >> 2;
+    r_kc[i] = (c & 3) * 8;
+    const int t = t0 + r_row[i], e = e0 + r_row[i];
     a_ptr[i] = t < T ? x + size_t(t) * d : nullptr;
-  }
-  // B: 128 rows x 8 float4 -> 4 float4 per thread
-  const float* b_ptr[4];
-  int b_k[4], b_row[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int c = tid + i * 256;
-    b_row[i] = c >> 3;
-    b_k[i] = (c & 7) * 4;
-    int e = e0 + b_row[i];
-    b_ptr[i] = e < E ? wr + size_t(e) * d : nullptr;
+    b_ptr[i] = e < E ? wsplit + size_t(e) * d : nullptr;
   }
 
-  uint4 ra[2];
-  float4 rb[4];
+  uint4 ra[2], rb[3][2];
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int k = k0 + a_kc[i];
-      ra[i] = (a_ptr[i] && k < d) ? *reinterpret_cast<const uint4*>(a_ptr[i] + k) : make_uint4(0, 0, 0, 0);
-    }
+      const int k = k0 + r_kc[i];
+      const bool ka = k < kend;  // d is a multiple of 8, so a chunk of 8 is all in or all out
+      ra[i] = (a_ptr[i] && ka) ? *reinterpret_cast<const uint4*>(a_ptr[i] + k) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int k = k0 + b_k[i];
-      rb[i] = (b_ptr[i] && k < d) ? *reinterpret_cast<const float4*>(b_ptr[i] + k)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < 3; ++p)
+        rb[p][i] = (b_ptr[i] && ka) ? *reinterpret_cast<const uint4*>(b_ptr[i] + p * part + k)
+                                    : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(&As[a_row[i] * LDA + a_kc[i]]) = ra[i];
+    for (int i = 0; i < 2; ++i) {
+      const int o = r_row[i] * LDA + r_kc[i];
+      *reinterpret_cast<uint4*>(&As[o]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16_t h[4], m[4], l[4];
-      split3(rb[i].x, h[0], m[0], l[0]);
-      split3(rb[i].y, h[1], m[1], l[1]);
-      split3(rb[i].z, h[2], m[2], l[2]);
-      split3(rb[i].w, h[3], m[3], l[3]);
-      int o = b_row[i] * LDA + b_k[i];
-      *reinterpret_cast<uint2*>(&Bs[0][o]) =
-          make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-      *reinterpret_cast<uint2*>(&Bs[1][o]) =
-          make_uint2(m[0] | (uint32_t(m[1]) << 16), m[2] | (uint32_t(m[3]) << 16));
-      *reinterpret_cast<uint2*>(&Bs[2][o]) =
-          make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+      for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(&Bs[p][o]) = rb[p][i];
     }
   };
 
@@ -112,13 +114,13 @@ __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (d + BK - 1) / BK;
-  load(0);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  load(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
     store();
     __syncthreads();
-    if (kt + 1 < nk) load((kt + 1) * BK);
+    if (kt + 1 < nk) load(kbeg + (kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kk = ks * 16 + lk;
@@ -269,13 +271,47 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
+// logits = sum of the split partials, added in split order (n = T*E, 4 per thread).
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ rpart,
+                                                            float* __restrict__ logits,
+                                                            int splits, size_t n) {
+  const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (n % 4 == 0 && i + 3 < n) {  // every partial array starts 16-byte aligned
+    float4 a = *reinterpret_cast<const float4*>(rpart + i);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = *reinterpret_cast<const float4*>(rpart + sp * n + i);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    *reinterpret_cast<float4*>(logits + i) = a;
+  } else {
+    for (size_t q = i; q < n && q < i + 4; ++q) {
+      float a = rpart[q];
+      for (int sp = 1; sp < splits; ++sp) a += rpart[sp * n + q];
+      logits[q] = a;
+    }
+  }
+}
+
 hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
-                                float* logits, hipStream_t st) {
+                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st) {
   const int E = s.N + s.Z;
   if (s.dtype == LC_MOE_BF16) {
-    dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM);
+    const size_t n = size_t(E) * s.d;  // a multiple of 8
+    hipLaunchKernelGGL(router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
+                       w_router, wsplit, n);
+    const RouterSplit rs = router_split(s);
+    dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM, rs.splits);
     hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(x), w_router, logits, s.T, s.d, E);
+                       static_cast<const bf16_t*>(x), wsplit, rs.splits > 1 ? rpart : logits,
+                       s.T, s.d, E, rs.chunk);
+    if (rs.splits > 1) {
+      const size_t nl = size_t(s.T) * E;
+      hipLaunchKernelGGL(router_reduce_kernel, dim3(unsigned((nl + 1023) / 1024)), dim3(256), 0, st,
+                         rpart, logits, rs.splits, nl);
+    }
   } else {
     dim3 grid((E + 63) / 64, (s.T + 63) / 64);
     hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(256), 0, st,
