@@ -19,7 +19,8 @@ beside it.  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZ
 (null) when the kernel source no longer matches the one the counters were taken on.
 decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
 (gate/up + down) is bound by streaming the weights of the experts that received at least
-one token; reported against the HBM peak.
+one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
+graph and replayed (graph_ms_per_step).
 cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -169,6 +170,36 @@ def cpu_baseline(st, wl, max_ffn_rows=1536):
                        f"elementwise numpy on 1 thread, BLAS on {blas_threads}")}
 
 
+def graph_ms(lm, st, steps):
+    """Capture one lc_moe_forward into a HIP graph (torch.cuda.CUDAGraph) and time `steps`
+    back-to-back replays with events; returns ms per replay."""
+    import torch
+    o = st["outs"]
+
+    def fwd():
+        lm.lc_moe_forward(st["shape"], st["x"], st["wts"], o["y"], o["idx"], o["gate"], o["load"], st["ws"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del g
+    return ms
+
+
 def decode_runs(lm, dev, steps, warmup):
     import torch
     from inputs import configs
@@ -183,13 +214,15 @@ def decode_runs(lm, dev, steps, warmup):
             wbytes = touched * 3 * wl.I * wl.d * 2
             ffn_ms = float(np.mean(stages["gate_up"]) + np.mean(stages["down"]))
             gbs = wbytes / (ffn_ms * 1e-3) / 1e9
+            gms = graph_ms(lm, st, steps)
             res.append({"T": T, "zero_share_pct": share, "ms_per_step": total / steps,
+                        "graph_ms_per_step": gms,
                         "tokens_per_s": T * steps / (total * 1e-3), "touched_experts": touched,
                         "ffn_rows": int(load[:wl.N].sum()), "ffn_ms": ffn_ms,
                         "ffn_weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                         "stages_ms": {k: float(np.mean(v)) for k, v in stages.items()}})
-            log(f"decode T={T} share={share}%: {total / steps:.3f} ms/step, FFN {ffn_ms:.3f} ms, "
-                f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+            log(f"decode T={T} share={share}%: {total / steps:.3f} ms/step ({gms:.3f} from a graph), "
+                f"FFN {ffn_ms:.3f} ms, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
             del st
             torch.cuda.empty_cache()
     return res
