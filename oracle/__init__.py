@@ -11,6 +11,9 @@ Modules:
               experts, combine (the reference every GPU result is compared against)
   bruteforce  scalar pure-Python formulation for tiny inputs (pins moe)
   dense       dense-masked formulation of the combine (pins moe's permute/combine)
+  controller  expert-bias PID controller (one update of the selection bias from loads)
+  fp8         block-FP8 expert weights: E4M3 encode/decode, power-of-two block scales,
+              quantize / dequantize
   tune_routing_inputs
               offline script: tunes the zero-expert bias shift and lists the tokens
               whose selection scores are too close to order reliably; writes
