@@ -20,7 +20,8 @@ beside it.  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZ
 decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
 (gate/up + down) is bound by streaming the weights of the experts that received at least
 one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
-graph and replayed (graph_ms_per_step).
+graph and replayed (graph_ms_per_step), and run on block-FP8 expert weights (fp8_*).
+prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
 cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -91,6 +92,14 @@ def setup(wl, dev):
     wts = lm._weights(wr, b, w["gate"], w["up"], w["down"])
     torch.cuda.synchronize()
     return dict(ri=ri, w=w, x=x, wr=wr, b=b, shape=shape, ws=ws, outs=outs, wts=wts)
+
+
+def use_fp8(lm, st):
+    """Quantize the layer's expert weights to block FP8 and point the forward at them."""
+    import torch
+    st["fp8"] = lm.quantize_weights(st["w"]["gate"], st["w"]["up"], st["w"]["down"])
+    st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"], st["fp8"])
+    torch.cuda.synchronize()
 
 
 def run_steps(lm, st, steps, warmup):
@@ -215,14 +224,21 @@ def decode_runs(lm, dev, steps, warmup):
             ffn_ms = float(np.mean(stages["gate_up"]) + np.mean(stages["down"]))
             gbs = wbytes / (ffn_ms * 1e-3) / 1e9
             gms = graph_ms(lm, st, steps)
+            use_fp8(lm, st)
+            total8, stages8 = run_steps(lm, st, steps, warmup)
+            ffn8 = float(np.mean(stages8["gate_up"]) + np.mean(stages8["down"]))
+            gbs8 = wbytes / 2 / (ffn8 * 1e-3) / 1e9  # FP8 codes: half the bytes (scales < 0.02%)
             res.append({"T": T, "zero_share_pct": share, "ms_per_step": total / steps,
-                        "graph_ms_per_step": gms,
+                        "graph_ms_per_step": gms, "fp8_ms_per_step": total8 / steps, "fp8_ffn_ms": ffn8,
+                        "fp8_ffn_weight_GBps": gbs8, "fp8_hbm_frac": gbs8 / HBM_PEAK_GBS,
                         "tokens_per_s": T * steps / (total * 1e-3), "touched_experts": touched,
                         "ffn_rows": int(load[:wl.N].sum()), "ffn_ms": ffn_ms,
                         "ffn_weight_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                         "stages_ms": {k: float(np.mean(v)) for k, v in stages.items()}})
             log(f"decode T={T} share={share}%: {total / steps:.3f} ms/step ({gms:.3f} from a graph), "
-                f"FFN {ffn_ms:.3f} ms, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+                f"FFN {ffn_ms:.3f} ms, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak); "
+                f"FP8 weights {total8 / steps:.3f} ms/step, FFN {ffn8:.3f} ms, {gbs8:.0f} GB/s "
+                f"({gbs8 / HBM_PEAK_GBS:.1%})")
             del st
             torch.cuda.empty_cache()
     return res
@@ -299,6 +315,16 @@ def main():
                 "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
         "stages_ms": st_ms,
     }
+    use_fp8(lm, st)
+    total8, stages8 = run_steps(lm, st, args.steps, args.warmup)
+    st8 = {k: float(np.mean(v)) for k, v in stages8.items()}
+    gu8_bytes = touched * 2.0 * wl.I * wl.d + nnz * (wl.d + wl.I) * 2.0
+    result["prefill_fp8"] = {"ms_per_step": total8 / args.steps, "tokens_per_s": wl.T * args.steps / (total8 * 1e-3),
+                             "stages_ms": st8,
+                             "gate_up_GBps": gu8_bytes / (st8["gate_up"] * 1e-3) / 1e9,
+                             "gate_up_tflops": gu_flops / (st8["gate_up"] * 1e-3) / 1e12}
+    log(f"FP8 weights: {total8 / args.steps:.3f} ms/step; stages "
+        f"{json.dumps({k: round(v, 4) for k, v in st8.items()})}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(st, wl)

@@ -72,6 +72,9 @@ typedef struct {
   const void* w_gate;    /* [N][I][d] dtype: SwiGLU gate projection of each FFN expert    */
   const void* w_up;      /* [N][I][d] dtype: SwiGLU up projection                        */
   const void* w_down;    /* [N][d][I] dtype: SwiGLU down projection                      */
+  const void* fp8;       /* NULL, or the block-FP8 expert weights made by
+                            lc_moe_quantize_weights; then the FFN uses them and w_gate,
+                            w_up, w_down are not read (they may be NULL)                 */
 } lc_moe_weights;
 
 /* Stages of lc_moe_forward, in launch order (names from lc_moe_stage_name). */
@@ -147,6 +150,29 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
                                     float* topk_gate, int32_t* load, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* stage_events);
+
+/* Block-FP8 expert weights.  The pages quantize with the fine-grained block scheme of
+ * DeepSeek-V3 (LongCat-Flash article, section "System-level optimisation", quantization
+ * paragraph) without fixing its details; this library takes: OCP FP8 E4M3 codes; one
+ * scale per block of 128 rows x 128 reduction columns of every expert matrix (partial
+ * blocks at the edges); the scale is a power of two, 2^k with k the smallest integer such
+ * that the block's largest |w| <= 448 * 2^k; each w / 2^k is rounded to the nearest E4M3
+ * value, ties to the even code.  Weights only: activations, H and Y stay bf16, and the
+ * layer computed is the bf16 layer with every expert weight replaced by code * 2^k (exact
+ * in bf16).  Blocks whose scale would fall below 2^-126 (max |w| < 448 * 2^-126) are
+ * outside the contract.
+ *
+ * lc_moe_fp8_weights_size: bytes of the packed form for this shape; 0 when the shape
+ * has none (fp32 layers, d or I not a multiple of 32, or d or I above 16384).
+ * lc_moe_quantize_weights: writes the packed form (an opaque tile layout the FFN streams
+ * plus the fp32 scales) of the bf16 W_gate, W_up [N][I][d] and W_down [N][d][I] into
+ * fp8_weights (fp8_weights_bytes >= lc_moe_fp8_weights_size, 16-byte aligned).  Pass it
+ * as lc_moe_weights.fp8.  Needs dtype LC_MOE_BF16 (else LC_MOE_E_DTYPE) and a shape
+ * with a packed form (else LC_MOE_E_SHAPE). */
+size_t lc_moe_fp8_weights_size(const lc_moe_shape* shape);
+lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* fp8_weights,
+                                      size_t fp8_weights_bytes, hipStream_t stream);
 
 /* PID gains of the expert-bias controller (host struct). */
 typedef struct {

@@ -118,6 +118,47 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   return p;
 }
 
+// XOR swizzle of the 16-byte chunk slot for 64-byte LDS rows: the 32 rows of one MFMA
+// operand read spread over all banks.
+__host__ __device__ __forceinline__ int swz4(int r) {
+  return (((r >> 1) & 1) << 1) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+}
+
+// Block-FP8 expert weights (E4M3 codes, one power-of-two scale per 128x128 block), packed
+// for the pipelined FFN kernel.  Regions (256-byte aligned, in this order):
+//   codes_gu  [N][ceil(I/128)][d/32][128 pair-rows][64 B]  pair-row p of n-tile nt holds
+//             W_gate row nt*128+p and W_up row nt*128+p (rows past I are zero)
+//   codes_d   [N][ceil(d/256)][I/32][128 pair-rows][64 B]  pair-row p of n-tile nt holds
+//             W_down rows nt*256 + (p/32)*64 + p%32 and that + 32 (rows past d: zero)
+//   scales_gu [N][2][ceil(I/128)][ceil(d/128)] fp32     2^k of each gate (0) / up (1) block
+//   scales_d  [N][ceil(d/128)][ceil(I/128)] fp32        2^k of each W_down block
+// A pair-row is four 16-byte chunks; chunk g holds the codes of columns 8g..8g+7 (of the
+// 32) of its first row, then of its second row, and sits in slot g ^ swz4(p).  A wave's
+// two weight blocks thus come from one 16-byte LDS read per lane, and the 32 pair-rows of
+// one read hit distinct banks.
+struct Fp8Plan {
+  size_t codes_gu, codes_d, scales_gu, scales_d, total;
+  int nt_gu, nt_d, nrb_i, nrb_d;  // n-tiles of gate/up and down; 128-row blocks of I and d
+};
+inline Fp8Plan plan_fp8(const lc_moe_shape& s) {
+  Fp8Plan p{};
+  // the kernel keeps a row of up to 128 column-block scales in two registers per lane
+  if (!ffn_pipelined(s) || s.d > 16384 || s.I > 16384) return p;
+  const size_t N = s.N;
+  p.nt_gu = (s.I + 127) / 128;
+  p.nt_d = (s.d + 255) / 256;
+  p.nrb_i = (s.I + 127) / 128;
+  p.nrb_d = (s.d + 127) / 128;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  p.codes_gu = take(N * p.nt_gu * size_t(s.d / 32) * 8192);
+  p.codes_d = take(N * p.nt_d * size_t(s.I / 32) * 8192);
+  p.scales_gu = take(N * 2 * size_t(p.nrb_i) * p.nrb_d * 4);
+  p.scales_d = take(N * size_t(p.nrb_d) * p.nrb_i * 4);
+  p.total = o;
+  return p;
+}
+
 // ---- launchers (host functions defined in the .hip files) ------------------------------
 
 // Router logits L[T][E] = x W_r^T (fp32 result).  bf16 layers: W_r is first split into
@@ -148,13 +189,20 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t st);
 
 // Grouped SwiGLU FFN over the FFN picks.
+// With fp8 != nullptr (packed block-FP8 weights, pipelined shapes only) the weights come
+// from it and w_gate / w_up / w_down are not read.
 hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
-                              const void* w_gate, const void* w_up, void* hbuf,
+                              const void* w_gate, const void* w_up, const void* fp8, void* hbuf,
                               const MTile* mtiles, const int32_t* offsets,
                               const int32_t* n_mtiles, int mt_max, hipStream_t st);
 hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
-                           void* ybuf, const MTile* mtiles, const int32_t* offsets,
-                           const int32_t* n_mtiles, int mt_max, hipStream_t st);
+                           const void* fp8, void* ybuf, const MTile* mtiles,
+                           const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
+                           hipStream_t st);
+// Quantize bf16 W_gate, W_up [N][I][d] and W_down [N][d][I] into the packed block-FP8
+// form (plan_fp8) at `out`.
+hipError_t launch_quantize_weights(const lc_moe_shape& s, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* out, hipStream_t st);
 
 // y_t = sum_k g_tk * (FFN row or x_t), k ascending, fp32 accumulation.
 hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,

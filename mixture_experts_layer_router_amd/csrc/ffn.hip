@@ -215,21 +215,18 @@ __global__ __launch_bounds__(256, 2) void ffn_bf16_kernel(
 //   MODE 1 (down):    weight rows = W_down rows n0..n0+255; activations = H rows;
 //                     epilogue -> Y (256 columns per tile).
 // Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4) through a
-// 4-stage ring (4 x 36 KB); activation row groups past the tile's rows are not loaded.
+// 160 KB ring whose stage holds the tile's activation rows (rounded up to 32) and the 256
+// weight rows, so few-row tiles get more stages; activation row groups past the tile's
+// rows are not loaded.
 // LDS row = 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits in slot c ^ swz(r).
 // Software pipeline: a K step has two substeps of 16 (one MFMA deep).  While one substep
 // multiplies, the wave reads all its fragments of the next substep into the other
 // register set.  Between the substeps of step kt each wave waits for its own LDS reads and
 // for its share of stage kt+1, then meets the others at a barrier; past it no wave reads
-// stage kt again, so the second substep refills stage kt's slot with stage kt+4, four
+// stage kt again, so the second substep refills stage kt's slot with stage kt+NST, NST
 // steps ahead of its use.
 // ---------------------------------------------------------------------------------------
 
-// XOR swizzle of the 16-byte chunk slot for 64-byte LDS rows: the 32 rows of one MFMA
-// operand read spread over all banks.
-__device__ __forceinline__ int swz4(int r) {
-  return (((r >> 1) & 1) << 1) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -249,25 +246,46 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int MODE>
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes -> 8 bf16 values code * scale (scale a power of two: exact).
+__device__ __forceinline__ bf16x8 dequant8(uint2 q, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, scale, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, scale, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, scale, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, scale, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// FP8 = false: weights bf16 row-major (w0, w1).  FP8 = true: weights are the packed
+// block-FP8 codes (qcodes: this matrix pair's region, one 8 KB tile block per stage) with
+// fp32 power-of-two scales (qscales; nrb_rows row blocks x nkb column blocks per matrix);
+// each weight fragment is converted to bf16 (v_cvt_scalef32_pk_bf16_fp8, exact) right
+// before its MFMAs, so the MFMAs see exactly the dequantized weights.
+template <int MODE, bool FP8>
 __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     const bf16_t* __restrict__ a_src, const int32_t* __restrict__ perm_token,
-    const bf16_t* __restrict__ w0, const bf16_t* __restrict__ w1, bf16_t* __restrict__ out,
-    const MTile* __restrict__ mtiles, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ n_mtiles_ptr, int kdim, int ncols, int n_ntiles) {
+    const bf16_t* __restrict__ w0, const bf16_t* __restrict__ w1,
+    const unsigned char* __restrict__ qcodes, const float* __restrict__ qscales, int nrb_rows,
+    int nkb, bf16_t* __restrict__ out, const MTile* __restrict__ mtiles,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_mtiles_ptr, int kdim,
+    int ncols, int n_ntiles) {
   constexpr int BM = kBmPipe;             // 320
-  constexpr int BK = 32, NST = 4;         // K step, ring stages
-  constexpr int LEAD = NST;               // stages loaded ahead of the one multiplied
+  constexpr int BK = 32;                  // K step
+  constexpr int LDS_BYTES = 160 * 1024;   // the ring
+  constexpr int MAX_NST = 16;             // ring stages at most
   constexpr int MB = BM / 64;             // row blocks per wave (5)
-  constexpr int RB = BK * 2;              // bytes per LDS row (64)
+  constexpr int RB = BK * 2;              // bytes per LDS activation row (64)
   constexpr int RPI = 16;                 // rows filled by one wave-wide load
   constexpr int NIA = BM / RPI;           // activation loads per stage (20)
-  constexpr int NIB = 256 / RPI;          // weight loads per stage (16)
+  constexpr int NIB = FP8 ? 8 : 256 / RPI;  // weight loads per stage (8 of 32 FP8 rows, 16)
   constexpr int IA = (NIA + 7) / 8;       // activation load slots per wave (3)
-  constexpr int IB = NIB / 8;             // weight loads per wave (2)
-  constexpr int A_BYTES = BM * RB;
-  constexpr int STAGE = A_BYTES + 256 * RB;  // 36 KB
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+  constexpr int IB = NIB / 8;             // weight loads per wave (1, 2)
+  constexpr int B_BYTES = FP8 ? 256 * 32 : 256 * RB;  // 8 KB / 16 KB
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
   int j, ntile;
   if (!unit_of_block(mtiles, offsets, *n_mtiles_ptr, n_ntiles, BM, j, ntile)) return;
@@ -295,20 +313,29 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     const size_t src_row = MODE == 0 ? size_t(perm_token[row0 + ar]) : size_t(row0 + ar);
     srcA[i] = a_src + src_row * kdim + (lslot ^ swz4(r)) * 8;
   }
+  // FP8: weight load q is the 1 KB piece q of the stage's 8 KB tile block, copied as is.
+  // (addressed through a bf16_t pointer like the other weight loads, so the compiler's
+  // alias view of these loads matches theirs and it adds no waits of its own)
+  const bf16_t* srcQ = nullptr;
+  if (FP8) {
+    srcQ = reinterpret_cast<const bf16_t*>(qcodes + (size_t(e) * n_ntiles + ntile) * (kdim / BK) * size_t(8192) +
+                                           wave * 1024 + lane * 16);
+  } else {
 #pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int r = (wave + 8 * i) * RPI + lrow;  // weight row of the tile, 0..255
-    int c;
-    const bf16_t* mat;
-    if (MODE == 0) {
-      c = n0 + (r & 127);
-      mat = r < 128 ? w0 : w1;
-    } else {
-      c = n0 + r;
-      mat = w0;
+    for (int i = 0; i < IB; ++i) {
+      const int r = (wave + 8 * i) * RPI + lrow;  // weight row of the tile, 0..255
+      int c;
+      const bf16_t* mat;
+      if (MODE == 0) {
+        c = n0 + (r & 127);
+        mat = r < 128 ? w0 : w1;
+      } else {
+        c = n0 + r;
+        mat = w0;
+      }
+      const int brow = c < ncols ? c : n0;  // columns past the matrix repeat a valid row
+      srcB[i] = mat + (size_t(e) * ncols + brow) * kdim + (lslot ^ swz4(r)) * 8;
     }
-    const int brow = c < ncols ? c : n0;  // columns past the matrix repeat a valid row
-    srcB[i] = mat + (size_t(e) * ncols + brow) * kdim + (lslot ^ swz4(r)) * 8;
   }
   const int per_stage = na + IB;  // this wave's loads per stage (vmcnt increments)
   const int nk = kdim / BK;
@@ -321,24 +348,38 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   const int krot = (j * 7 + ntile * 3) % nk;
 #endif
   auto kphys = [&](int kt) { const int k = kt + krot; return (k >= nk ? k - nk : k) * BK; };
-  // this wave's load number i (0..IA+IB-1) of stage kt
-  auto issue_one = [&](int i, int kt) {
-    unsigned char* st = smem + (kt % NST) * STAGE;
+  // Ring geometry from the tile's rows: a stage holds the activation rows the MFMAs read
+  // (rows rounded up to 32) and the 256 weight rows, and the ring has as many stages as
+  // fit in 160 KB, up to 16 (bf16 weights: 4 at 320 rows, 5 at 256, 8 for decode-sized
+  // tiles; FP8 weights: 5 at 320 rows, 14 for decode-sized tiles).  Loads run that many
+  // stages ahead, so few-row tiles keep more weight bytes in flight.
+  const int a_bytes = __builtin_amdgcn_readfirstlane(((rows + 31) & ~31) * RB);
+  const int stage_bytes = a_bytes + B_BYTES;
+  const int nst = LDS_BYTES / stage_bytes < MAX_NST ? LDS_BYTES / stage_bytes : MAX_NST;
+  // this wave's load number i (0..IA+IB-1) of stage kt, into ring slot `slot`
+  auto issue_one = [&](int i, int kt, int slot) {
+    unsigned char* st = smem + slot * stage_bytes;
     if (i < IA) {
       if (i < na) dma16(srcA[i] + kphys(kt), st + (wave + 8 * i) * 1024);
+    } else if (FP8) {
+      dma16(srcQ + size_t(kphys(kt)) * 128, st + a_bytes + wave * 1024);  // 8 KB per stage
     } else {
-      dma16(srcB[i - IA] + kphys(kt), st + A_BYTES + (wave + 8 * (i - IA)) * 1024);
+      dma16(srcB[i - IA] + kphys(kt), st + a_bytes + (wave + 8 * (i - IA)) * 1024);
     }
   };
-  // s_waitcnt vmcnt(n) for a run-time n (0..(LEAD-1)*(IA+IB))
+  // s_waitcnt vmcnt(n) for a run-time n.  The counter holds at most 63 loads, and a wave
+  // cannot issue a 64th, so a wait for a stage older than 63 later loads is already met.
   auto wait_vm = [&](int n) {
-    switch (n) {
+    switch (n < 63 ? n : 63) {
 #define LCM_CASE(k) case k: LCM_WAIT_VMCNT(k); break;
-      LCM_CASE(0) LCM_CASE(1) LCM_CASE(2) LCM_CASE(3) LCM_CASE(4) LCM_CASE(5) LCM_CASE(6)
-      LCM_CASE(7) LCM_CASE(8) LCM_CASE(9) LCM_CASE(10) LCM_CASE(11) LCM_CASE(12) LCM_CASE(13)
-      LCM_CASE(14)
+#define LCM_CASE8(k) LCM_CASE(k) LCM_CASE(k + 1) LCM_CASE(k + 2) LCM_CASE(k + 3) \
+                     LCM_CASE(k + 4) LCM_CASE(k + 5) LCM_CASE(k + 6) LCM_CASE(k + 7)
+      LCM_CASE8(0) LCM_CASE8(8) LCM_CASE8(16) LCM_CASE8(24) LCM_CASE8(32) LCM_CASE8(40)
+      LCM_CASE8(48) LCM_CASE(56) LCM_CASE(57) LCM_CASE(58) LCM_CASE(59) LCM_CASE(60)
+      LCM_CASE(61) LCM_CASE(62)
+#undef LCM_CASE8
 #undef LCM_CASE
-      default: LCM_WAIT_VMCNT(15); break;
+      default: LCM_WAIT_VMCNT(63); break;
     }
   };
   // wait until this wave's loads of stage s landed, `newest` being the last stage issued
@@ -348,7 +389,26 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   int boff[2];  // LDS byte offset of this lane's row in the wave's two weight blocks
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
-    boff[nb] = A_BYTES + ((MODE == 0 ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + l32) * RB;
+    boff[nb] = a_bytes + (FP8 ? (wn * 32 + l32) * 64  // FP8: pair-row wn*32 + l32 holds both blocks
+                              : ((MODE == 0 ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + l32) * RB);
+  // FP8 scales of the wave's two weight blocks (the rows of one 32-row weight block lie in
+  // one 128-row block): lane l holds the scale of column block l in vsc[nb][0] and of
+  // column block 64 + l in vsc[nb][1] (nkb <= 128), loaded once before the loads start;
+  // stage kt reads column block kphys(kt) / 128 from them with v_readlane.
+  float vsc[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
+  if (FP8) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int sbase = MODE == 0 ? ((e * 2 + nb) * nrb_rows + ntile) * nkb
+                                  : (e * nrb_rows + ntile * 2 + ((wn * 64 + nb * 32) >> 7)) * nkb;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = h * 64 + lane;
+        vsc[nb][h] = qscales[sbase + (kb < nkb ? kb : nkb - 1)];  // lanes past nkb: unused
+      }
+    }
+    LCM_WAIT_VMCNT(0);  // before the first direct load, so the vmcnt counts below hold
+  }
   int nvb = 0;  // row blocks of this wave holding tile rows (a prefix in mb)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) nvb += (mb * 2 + wm) * 32 < rows;
@@ -361,53 +421,100 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
 
-  const int npro = nk < LEAD ? nk : LEAD;
+  const int npro = nk < nst ? nk : nst;
   for (int s = 0; s < npro; ++s)
-    for (int i = 0; i < IA + IB; ++i) issue_one(i, s);
+    for (int i = 0; i < IA + IB; ++i) issue_one(i, s, s);
 
   auto run = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;  // row blocks holding tile rows
-    auto rd = [&](int kt, int ks, bf16x8 (&a)[MB], bf16x8 (&b)[2]) {
-      const unsigned char* st = smem + (kt % NST) * STAGE;
+    // Weight fragments as read from LDS; FP8: b[0] holds the codes of both blocks (the 16
+    // bytes of one read).  Every LDS operand read here has the bf16x8 type: the compiler's
+    // type-based alias analysis then keeps the reads apart from the LDS writes of the direct
+    // loads and it adds no waits of its own (the explicit vmcnt waits order them).  Reading
+    // the FP8 bytes as an integer vector made it wait for every load in flight before each
+    // read.
+    using BFrag = bf16x8;
+    auto rd = [&](int ring_slot, int ks, bf16x8 (&a)[MB], BFrag (&b)[2]) {
+      const unsigned char* st = smem + ring_slot * stage_bytes;
       const int slot = ((ks * 2 + khalf) ^ sw) * 16;
 #pragma unroll
       for (int mb = 0; mb < NV; ++mb)
         a[mb] = *reinterpret_cast<const bf16x8*>(st + ((mb * 2 + wm) * 32 + l32) * RB + slot);
+      if constexpr (FP8) {
+        // one 16-byte read: 8 codes of the block-0 row, then 8 codes of the block-1 row
+        b[0] = *reinterpret_cast<const bf16x8*>(st + boff[0] + slot);
+      } else {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = *reinterpret_cast<const bf16x8*>(st + boff[nb] + slot);
+        for (int nb = 0; nb < 2; ++nb) b[nb] = *reinterpret_cast<const bf16x8*>(st + boff[nb] + slot);
+      }
     };
-    // MFMAs of one substep; with DMA, this wave's loads of stage kt_load go one per row
-    // block, the rest after the last block.
-    auto mm = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[2], auto dma, int kt_load) {
+    // FP8 block scales of stage kt for the wave's two weight blocks
+    auto scales_of = [&](int kt, float (&sc)[2]) {
+      if constexpr (FP8) {
+        const int kb = __builtin_amdgcn_readfirstlane(kphys(kt) >> 7);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float v = kb < 64 ? vsc[nb][0] : vsc[nb][1];
+          sc[nb] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kb & 63));
+        }
+      }
+    };
+    // MFMAs of one substep; with DMA, this wave's loads of stage kt_load (into ring slot
+    // `slot`) go one per row block, the rest after the last block.
+    auto mm = [&](const bf16x8 (&a)[MB], const BFrag (&bq)[2], const float (&sc)[2], auto dma,
+                  int kt_load, int slot) {
       constexpr bool DMA = decltype(dma)::value;
+      bf16x8 b[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (FP8) {
+          if constexpr (NV > 0) {  // waves without rows skip it
+            const uint4 q = __builtin_bit_cast(uint4, bq[0]);
+            b[nb] = dequant8(nb == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w), sc[nb]);
+          }
+        } else {
+          b[nb] = bq[nb];
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < NV; ++mb) {
-        if (DMA && mb < IA + IB) issue_one(mb, kt_load);
+        if (DMA && mb < IA + IB) issue_one(mb, kt_load, slot);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
       }
       if (DMA)
-        for (int i = NV; i < IA + IB; ++i) issue_one(i, kt_load);
+        for (int i = NV; i < IA + IB; ++i) issue_one(i, kt_load, slot);
     };
-    bf16x8 ca[MB], cb[2], xa[MB], xb[2];  // fragments of the current / next substep
+    bf16x8 ca[MB], xa[MB];  // activation fragments of the current / next substep
+    BFrag cb[2], xb[2];     // weight fragments of the current / next substep
+    float sc[2] = {1.f, 1.f}, scn[2] = {1.f, 1.f};  // FP8 scales of stages kt / kt+1
+    scales_of(0, sc);
     wait_stage(0, npro - 1);
     block_barrier();
     rd(0, 0, ca, cb);
+    int sk = 0;  // ring slot of stage kt
     auto step = [&](int kt, auto more_tag, auto last_tag) {
       constexpr bool LAST = decltype(last_tag)::value;
-      rd(kt, 1, xa, xb);
-      mm(ca, cb, std::false_type{}, 0);
+      const int sk1 = sk + 1 == nst ? 0 : sk + 1;  // slot of stage kt+1
+      if (!LAST) scales_of(kt + 1, scn);
+      rd(sk, 1, xa, xb);
+      mm(ca, cb, sc, std::false_type{}, 0, 0);
       if (!LAST) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt done
-        const int newest = kt + LEAD - 1 < nk - 1 ? kt + LEAD - 1 : nk - 1;
+        const int newest = kt + nst - 1 < nk - 1 ? kt + nst - 1 : nk - 1;
         wait_stage(kt + 1, newest);
         block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again
-        rd(kt + 1, 0, ca, cb);
+        rd(sk1, 0, ca, cb);
       }
-      mm(xa, xb, more_tag, kt + LEAD);
+      mm(xa, xb, sc, more_tag, kt + nst, sk);  // stage kt+nst takes stage kt's slot
+      sk = sk1;
+      if (!LAST) {
+        sc[0] = scn[0];
+        sc[1] = scn[1];
+      }
     };
-    const int nmain = nk - LEAD > 0 ? nk - LEAD : 0;
+    const int nmain = nk - nst > 0 ? nk - nst : 0;
     for (int kt = 0; kt < nmain; ++kt) step(kt, std::true_type{}, std::false_type{});
     for (int kt = nmain; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
     step(nk - 1, std::false_type{}, std::true_type{});
@@ -449,14 +556,17 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   }
 }
 
-template __global__ void ffn_bf16_pipe_kernel<0>(
-    const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,
-    const bf16_t* __restrict__, bf16_t* __restrict__, const MTile* __restrict__,
-    const int32_t* __restrict__, const int32_t* __restrict__, int, int, int);
-template __global__ void ffn_bf16_pipe_kernel<1>(
-    const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,
-    const bf16_t* __restrict__, bf16_t* __restrict__, const MTile* __restrict__,
-    const int32_t* __restrict__, const int32_t* __restrict__, int, int, int);
+#define LCM_INST(M, Q)                                                                        \
+  template __global__ void ffn_bf16_pipe_kernel<M, Q>(                                        \
+      const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,    \
+      const bf16_t* __restrict__, const unsigned char* __restrict__, const float* __restrict__, \
+      int, int, bf16_t* __restrict__, const MTile* __restrict__, const int32_t* __restrict__, \
+      const int32_t* __restrict__, int, int, int);
+LCM_INST(0, false)
+LCM_INST(1, false)
+LCM_INST(0, true)
+LCM_INST(1, true)
+#undef LCM_INST
 
 // ---------------------------------------------------------------------------------------
 // fp32 kernel (FMA): tile 64 rows x 64 output columns, K step 16, 4x4 outputs per thread.
@@ -520,17 +630,25 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
 }
 
 hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
-                              const void* w_gate, const void* w_up, void* hbuf,
+                              const void* w_gate, const void* w_up, const void* fp8, void* hbuf,
                               const MTile* mtiles, const int32_t* offsets,
                               const int32_t* n_mtiles, int mt_max, hipStream_t st) {
   if (s.dtype == LC_MOE_BF16 && ffn_pipelined(s)) {
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
     const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
-    ffn_bf16_pipe_kernel<0><<<dim3(grid), dim3(512), 0, st>>>(
-        static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
-        static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
-        s.I, nn);
+    const Fp8Plan q = plan_fp8(s);
+    const unsigned char* qb = static_cast<const unsigned char*>(fp8);
+    if (fp8)
+      ffn_bf16_pipe_kernel<0, true><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(x), perm_token, nullptr, nullptr, qb + q.codes_gu,
+          reinterpret_cast<const float*>(qb + q.scales_gu), q.nrb_i, q.nrb_d,
+          static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn);
+    else
+      ffn_bf16_pipe_kernel<0, false><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
+          static_cast<const bf16_t*>(w_up), nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf),
+          mtiles, offsets, n_mtiles, s.d, s.I, nn);
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
@@ -552,15 +670,25 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
 }
 
 hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
-                           void* ybuf, const MTile* mtiles, const int32_t* offsets,
-                           const int32_t* n_mtiles, int mt_max, hipStream_t st) {
+                           const void* fp8, void* ybuf, const MTile* mtiles,
+                           const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
+                           hipStream_t st) {
   if (s.dtype == LC_MOE_BF16 && ffn_pipelined(s)) {
     const int nn = (s.d + 255) / 256;
     const size_t units = size_t(mt_max) * nn;
     const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
-    ffn_bf16_pipe_kernel<1><<<dim3(grid), dim3(512), 0, st>>>(
-        static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
-        static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn);
+    const Fp8Plan q = plan_fp8(s);
+    const unsigned char* qb = static_cast<const unsigned char*>(fp8);
+    if (fp8)
+      ffn_bf16_pipe_kernel<1, true><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(hbuf), nullptr, nullptr, nullptr, qb + q.codes_d,
+          reinterpret_cast<const float*>(qb + q.scales_d), q.nrb_d, q.nrb_i,
+          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn);
+    else
+      ffn_bf16_pipe_kernel<1, false><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
+          nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d,
+          nn);
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.d + 255) / 256;
     const size_t units = size_t(mt_max) * nn;

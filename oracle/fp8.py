@@ -78,15 +78,12 @@ def quantize(w):
     w = np.asarray(w, np.float64)
     R, C = w.shape
     nrb, ncb = -(-R // BLOCK), -(-C // BLOCK)
-    codes = np.empty((R, C), np.uint8)
-    ks = np.empty((nrb, ncb), np.int64)
-    for i in range(nrb):
-        for j in range(ncb):
-            blk = w[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK]
-            k = block_exponent(float(np.abs(blk).max()))
-            ks[i, j] = k
-            codes[i * BLOCK:(i + 1) * BLOCK, j * BLOCK:(j + 1) * BLOCK] = e4m3_encode(blk / 2.0 ** k)
-    return codes, ks
+    pad = np.zeros((nrb * BLOCK, ncb * BLOCK))
+    pad[:R, :C] = np.abs(w)
+    amax = pad.reshape(nrb, BLOCK, ncb, BLOCK).max(axis=(1, 3))
+    ks = np.array([[block_exponent(float(a)) for a in row] for row in amax], np.int64)
+    scale = np.repeat(np.repeat(2.0 ** ks, BLOCK, axis=0), BLOCK, axis=1)[:R, :C]
+    return e4m3_encode(w / scale), ks
 
 
 def dequantize(codes, ks):

@@ -14,12 +14,12 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "lc
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lc_moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(lc_moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -111,3 +111,18 @@ def test_bias_update_validation():
     assert f(ctypes.byref(s), ctypes.byref(g), P, MIS, P, P, P, None) == 4
     assert f(ctypes.byref(lm.make_shape(64, 128, 8, 4, 13, 256, lm.BF16)), ctypes.byref(g), P, P, P, P, P,
              None) == 2
+
+
+def test_fp8_size_and_quantize_validation():
+    s = lm.make_shape(T=64, d=128, N=8, Z=4, K=2, I=256, dtype=lm.BF16)
+    n = lm.lc_moe_fp8_weights_size(s)
+    # codes (one byte per weight, gate/up n-tiles of 128 rows, down n-tiles of 256) + scales
+    assert n >= 8 * (2 * 256 * 128 + 256 * 256) and n % 256 == 0
+    assert lm.lc_moe_fp8_weights_size(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)) == 0
+    assert lm.lc_moe_fp8_weights_size(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)) == 0  # d % 32
+    f = lm.lib().lc_moe_quantize_weights
+    assert f(ctypes.byref(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)), P, P, P, P, n, None) == 3
+    assert f(ctypes.byref(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)), P, P, P, P, n, None) == 2
+    assert f(ctypes.byref(s), None, P, P, P, n, None) == 1
+    assert f(ctypes.byref(s), P, P, MIS, P, n, None) == 4
+    assert f(ctypes.byref(s), P, P, P, P, n - 1, None) == 5
