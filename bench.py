@@ -22,6 +22,8 @@ decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); t
 one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
 graph and replayed (graph_ms_per_step), and run on block-FP8 expert weights (fp8_*).
 prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
+overlap: a dense SwiGLU FFN (width 2d) over the same tokens beside the layer, serial on one
+stream against concurrent on two streams.
 cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -209,6 +211,73 @@ def graph_ms(lm, st, steps):
     return ms
 
 
+def dense_ffn_setup(lm, wl, dev, i_dense):
+    """A dense SwiGLU FFN over all T tokens (width i_dense), expressed as the layer with one
+    FFN expert, no zero experts and K = 1: the router over one expert gives gate 1 exactly,
+    so y = FFN(x).  Returns (shape, weights, workspace, outputs)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    std = 1.0 / np.sqrt(wl.d)
+    w = {k: (torch.randn(sh, generator=g, device=dev) * std).to(torch.bfloat16)
+         for k, sh in (("gate", (1, i_dense, wl.d)), ("up", (1, i_dense, wl.d)), ("down", (1, wl.d, i_dense)))}
+    wr = torch.zeros((1, wl.d), dtype=torch.float32, device=dev)
+    b = torch.zeros(1, dtype=torch.float32, device=dev)
+    shape = lm.make_shape(wl.T, wl.d, 1, 0, 1, i_dense, lm.BF16)
+    ws = lm.workspace_for(shape, dev)
+    outs = dict(y=torch.empty((wl.T, wl.d), dtype=torch.bfloat16, device=dev),
+                idx=torch.empty((wl.T, 1), dtype=torch.int32, device=dev),
+                gate=torch.empty((wl.T, 1), dtype=torch.float32, device=dev),
+                load=torch.empty(1, dtype=torch.int32, device=dev))
+    return shape, lm._weights(wr, b, w["gate"], w["up"], w["down"]), ws, outs, w
+
+
+def overlap_run(lm, st, wl, steps, i_dense):
+    """The MoE layer and a dense FFN over the same tokens, one after the other on one
+    stream, then concurrently on two streams (default priority).  Returns ms per step."""
+    import torch
+    dev = st["x"].device
+    dshape, dwts, dws, douts, _keep = dense_ffn_setup(lm, wl, dev, i_dense)
+    o = st["outs"]
+
+    def moe(stream):
+        lm.lc_moe_forward(st["shape"], st["x"], st["wts"], o["y"], o["idx"], o["gate"], o["load"], st["ws"],
+                          stream=stream)
+
+    def dense(stream):
+        lm.lc_moe_forward(dshape, st["x"], dwts, douts["y"], douts["idx"], douts["gate"], douts["load"], dws,
+                          stream=stream)
+
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(s0)
+        for _ in range(steps):
+            fn()
+        b.record(s0)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    t_moe = timed(lambda: moe(s0))
+    t_dense = timed(lambda: dense(s0))
+    t_serial = timed(lambda: (moe(s0), dense(s0)))
+
+    def both():
+        s1.wait_stream(s0)
+        moe(s0)
+        dense(s1)
+        s0.wait_stream(s1)
+
+    t_conc = timed(both)
+    return {"dense_I": i_dense, "moe_ms": t_moe, "dense_ms": t_dense, "serial_ms": t_serial,
+            "concurrent_ms": t_conc, "saved_frac": 1.0 - t_conc / t_serial}
+
+
 def decode_runs(lm, dev, steps, warmup):
     import torch
     from inputs import configs
@@ -252,6 +321,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the dense-FFN-beside-the-layer two-stream measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -325,6 +396,12 @@ def main():
                              "gate_up_tflops": gu_flops / (st8["gate_up"] * 1e-3) / 1e12}
     log(f"FP8 weights: {total8 / args.steps:.3f} ms/step; stages "
         f"{json.dumps({k: round(v, 4) for k, v in st8.items()})}")
+    st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"])
+    if not args.no_overlap:
+        result["overlap"] = overlap_run(lm, st, wl, max(3, args.steps // 2), 2 * wl.d)
+        ov = result["overlap"]
+        log(f"dense FFN (I={ov['dense_I']}) beside the layer: moe {ov['moe_ms']:.3f} + dense {ov['dense_ms']:.3f} ms; "
+            f"serial {ov['serial_ms']:.3f} ms, two streams {ov['concurrent_ms']:.3f} ms ({ov['saved_frac']:.1%} saved)")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(st, wl)
