@@ -43,7 +43,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_gate_up_prefill_T16384_hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_router_amd", "csrc", f)
-                  for f in ("ffn.hip", "common.h")]
+                  for f in ("ffn.hip", "common.h", "lds_dma.h")]
 METRIC = "MoE-layer tokens/s and % of bf16 MFMA peak (prefill) / % HBM peak (decode)"
 
 

@@ -54,18 +54,30 @@ struct MTile {
   int expert, row0, rows, first_tile;
 };
 
-// Split-K of the bf16 router GEMM.  Its tiles are 128 tokens x 128 experts; when the
-// layer has few tokens (decode) there are too few tiles to fill 256 CUs, so the reduction
-// over d is cut into `splits` chunks of `chunk` columns (a multiple of 32) whose partial
-// logits are summed, in chunk order, by a reduction kernel.
+// bf16 router GEMM tiles.  With d a multiple of 32 the pipelined kernel runs, on tiles of
+// kRouterBm tokens x kRouterBe experts, one workgroup per CU; otherwise the 128 x 128
+// kernel, two workgroups per CU.
+constexpr int kRouterBm = 256, kRouterBe = 192;
+inline bool router_pipelined(const lc_moe_shape& s) {
+  return s.dtype == LC_MOE_BF16 && s.d % 32 == 0;
+}
+
+// Split-K of the bf16 router GEMM.  When the layer has few tokens (decode) there are too
+// few tiles to fill 256 CUs, so the reduction over d is cut into `splits` chunks of
+// `chunk` columns (a multiple of 32) whose partial logits are summed, in chunk order, by a
+// reduction kernel.
 struct RouterSplit {
   int splits, chunk;
 };
 inline RouterSplit router_split(const lc_moe_shape& s) {
   RouterSplit r{1, s.d};
   if (s.dtype != LC_MOE_BF16) return r;
-  const long long tiles = (long long)((s.N + s.Z + 127) / 128) * ((s.T + 127) / 128);
-  long long want = (512 + tiles - 1) / tiles;
+  const int E = s.N + s.Z;
+  const bool pipe = router_pipelined(s);
+  const long long tiles = pipe ? (long long)((E + kRouterBe - 1) / kRouterBe) * ((s.T + kRouterBm - 1) / kRouterBm)
+                               : (long long)((E + 127) / 128) * ((s.T + 127) / 128);
+  const long long slots = pipe ? 256 : 512;  // workgroups the chip holds at once
+  long long want = (slots + tiles - 1) / tiles;
   const int kmax = (s.d + 31) / 32;
   if (want > kmax) want = kmax;
   if (want <= 1) return r;

@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lds_dma.h"
 
 namespace lcm {
 
@@ -227,25 +228,6 @@ __global__ __launch_bounds__(256, 2) void ffn_bf16_kernel(
 // steps ahead of its use.
 // ---------------------------------------------------------------------------------------
 
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wave-wide direct global->LDS load: lane l copies 16 bytes from g to lds + 16*l.
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-#define LCM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
-
-// Workgroup barrier without the vmcnt(0) that __syncthreads implies: the direct loads of
-// later stages stay in flight across it.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // 8 E4M3 codes -> 8 bf16 values code * scale (scale a power of two: exact).
@@ -367,23 +349,8 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
       dma16(srcB[i - IA] + kphys(kt), st + a_bytes + (wave + 8 * (i - IA)) * 1024);
     }
   };
-  // s_waitcnt vmcnt(n) for a run-time n.  The counter holds at most 63 loads, and a wave
-  // cannot issue a 64th, so a wait for a stage older than 63 later loads is already met.
-  auto wait_vm = [&](int n) {
-    switch (n < 63 ? n : 63) {
-#define LCM_CASE(k) case k: LCM_WAIT_VMCNT(k); break;
-#define LCM_CASE8(k) LCM_CASE(k) LCM_CASE(k + 1) LCM_CASE(k + 2) LCM_CASE(k + 3) \
-                     LCM_CASE(k + 4) LCM_CASE(k + 5) LCM_CASE(k + 6) LCM_CASE(k + 7)
-      LCM_CASE8(0) LCM_CASE8(8) LCM_CASE8(16) LCM_CASE8(24) LCM_CASE8(32) LCM_CASE8(40)
-      LCM_CASE8(48) LCM_CASE(56) LCM_CASE(57) LCM_CASE(58) LCM_CASE(59) LCM_CASE(60)
-      LCM_CASE(61) LCM_CASE(62)
-#undef LCM_CASE8
-#undef LCM_CASE
-      default: LCM_WAIT_VMCNT(63); break;
-    }
-  };
   // wait until this wave's loads of stage s landed, `newest` being the last stage issued
-  auto wait_stage = [&](int s, int newest) { wait_vm((newest - s) * per_stage); };
+  auto wait_stage = [&](int s, int newest) { wait_vmcnt((newest - s) * per_stage); };
 
   const int l32 = lane & 31, sw = swz4(l32), khalf = lane >> 5;
   int boff[2];  // LDS byte offset of this lane's row in the wave's two weight blocks
@@ -501,7 +468,7 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
       rd(sk, 1, xa, xb);
       mm(ca, cb, sc, std::false_type{}, 0, 0);
       if (!LAST) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt done
+        wait_lds_reads();  // this wave's reads of stage kt done
         const int newest = kt + nst - 1 < nk - 1 ? kt + nst - 1 : nk - 1;
         wait_stage(kt + 1, newest);
         block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again

@@ -12,7 +12,10 @@
 //   fp32 x: plain fp32 FMA, LDS-tiled.
 // Stage 2 (top-K): one wavefront per token: max, exp, sum and divide in fp32, then K
 //   rounds of a wavefront argmax over s = p + b (ties -> lower index) by shuffles.
+#include <type_traits>
+
 #include "common.h"
+#include "lds_dma.h"
 
 namespace lcm {
 
@@ -156,6 +159,191 @@ __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
         if (t < T) logits[size_t(t) * E + e] = acc[i][j][r];
       }
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// Pipelined bf16 MFMA logits (d a multiple of 32).  Tile: 256 tokens x 192 experts, K step
+// 32.  The weight operand is the tile's 3 x 192 = 576 part rows (all hi rows, then all
+// mid rows, then all lo rows).  512 threads = 8 waves; wave w owns token blocks
+// 2*(w >> 1) + {0, 1} against expert blocks 3*(w & 1) + {0, 1, 2}: 2 x 3 blocks of 32x32,
+// three MFMAs per block and 16-wide substep (hi, mid, lo: the same order of additions as
+// the 128 x 128 kernel), 96 fp32 accumulators per lane.
+// Operands reach LDS by direct global->LDS loads into a 3-stage ring (52 KB a stage, 64
+// bytes per row, chunk c of row r in slot c ^ swz4(r)).  A K step has two substeps of 16;
+// between them each wave waits for its own loads of stage kt+1 and meets the others at a
+// barrier, past which no wave reads stage kt again, so the second substep refills that
+// slot with stage kt+3.  Token row groups past T are not loaded and waves skip the MFMAs
+// of token blocks past T.
+// Work unit = (token tile, expert tile, K chunk), ordered token tile, expert tile, chunk;
+// workgroup w runs on XCD w % 8 and each XCD takes one contiguous eighth of the units, so
+// the expert tiles of one token tile run side by side on one XCD and share its
+// activation rows in that XCD's L2.
+// ---------------------------------------------------------------------------------------
+namespace rp {
+constexpr int BM = kRouterBm, BE = kRouterBe, NP = 3, BK = 32, RB = BK * 2;
+constexpr int BROWS = NP * BE;             // 576 part rows
+constexpr int A_BYTES = BM * RB;           // 16 KB
+constexpr int STAGE = (BM + BROWS) * RB;   // 52 KB
+constexpr int NST = 3;                     // ring stages
+constexpr int NL = (BM + BROWS) / 16;      // wave-wide loads per stage (52)
+constexpr int LPW = (NL + 7) / 8;          // load slots per wave (7)
+}
+
+__global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, float* __restrict__ out,
+    int T, int d, int E, int chunk, int n_et, int splits, int n_units) {
+  using namespace rp;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+
+  const int per = (n_units + 7) >> 3;
+  const int wslot = blockIdx.x >> 3;
+  if (wslot >= per) return;
+  const int u = (blockIdx.x & 7) * per + wslot;
+  if (u >= n_units) return;
+  const int sp = u % splits;
+  const int et = (u / splits) % n_et;
+  const int tt = u / (splits * n_et);
+  const int t0 = tt * BM, e0 = et * BE;
+  const int kbeg = sp * chunk;
+  const int kend = kbeg + chunk < d ? kbeg + chunk : d;
+  const int nk = (kend - kbeg) / BK;
+  const int rows = T - t0 < BM ? T - t0 : BM;  // tokens of this tile
+  float* logits = out + size_t(sp) * T * E;
+  const size_t part = size_t(E) * d;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Load q (0..51) belongs to wave q % 8 and fills stage rows 16q..16q+15 (rows 0..255:
+  // tokens, 256..831: part rows); lane l fills row 16q + l/4, slot l%4, with global chunk
+  // (l%4) ^ swz4(row).  Token loads whose 16 rows all lie past T are skipped.
+  const bf16_t* src[LPW];
+  int lmask = 0;  // bit i: this wave issues its load i
+  const int lrow = lane >> 2, lslot = lane & 3;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = wave + 8 * i;
+    const int r = q * 16 + lrow;  // stage row
+    const bf16_t* p = x;
+    if (q < BM / 16) {
+      if (q * 16 < rows) lmask |= 1 << i;
+      const int t = r < rows ? t0 + r : t0;  // rows past T read a valid row; never stored
+      p = x + size_t(t) * d;
+    } else if (q < NL) {
+      lmask |= 1 << i;
+      const int br = r - BM, pp = br / BE, c = e0 + br % BE;
+      p = wsplit + pp * part + size_t(c < E ? c : e0) * d;  // experts past E: a valid row
+    }
+    src[i] = p + kbeg + (lslot ^ swz4(r)) * 8;
+  }
+  const int nl = __builtin_popcount(lmask);  // this wave's loads per stage
+  auto issue_one = [&](int i, int kt, int slot) {
+    if ((lmask >> i) & 1) dma16(src[i] + kt * BK, smem + slot * STAGE + (wave + 8 * i) * 1024);
+  };
+  auto wait_stage = [&](int s, int newest) { wait_vmcnt((newest - s) * nl); };
+
+  const int l32 = lane & 31, sw = swz4(l32), khalf = lane >> 5;
+  int nvb = 0;  // token blocks of this wave holding tokens (a prefix)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) nvb += (wm * 2 + mb) * 32 < rows;
+
+  f32x16 acc[2][3];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+  const int npro = nk < NST ? nk : NST;
+  for (int s = 0; s < npro; ++s) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) issue_one(i, s, s);
+  }
+
+  auto run = [&](auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;
+    // fragments of one substep: a[mb] tokens, b[p][nb] part p of expert block nb
+    auto rd = [&](int ring_slot, int ks, bf16x8 (&a)[2], bf16x8 (&b)[3][3]) {
+      const unsigned char* st = smem + ring_slot * STAGE;
+      const int cs = ((ks * 2 + khalf) ^ sw) * 16;
+#pragma unroll
+      for (int mb = 0; mb < NV; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(st + ((wm * 2 + mb) * 32 + l32) * RB + cs);
+      if (NV > 0) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int nb = 0; nb < 3; ++nb)
+            b[p][nb] = *reinterpret_cast<const bf16x8*>(
+                st + (BM + p * BE + (wn * 3 + nb) * 32 + l32) * RB + cs);
+      }
+    };
+    // MFMAs of one substep; with DMA, this wave's loads of stage kt_load (ring slot `slot`)
+    // go one per block, the rest after the last block.
+    auto mm = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[3][3], auto dma, int kt_load, int slot) {
+      constexpr bool DMA = decltype(dma)::value;
+#pragma unroll
+      for (int mb = 0; mb < NV; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 3; ++nb) {
+          if (DMA && mb * 3 + nb < LPW) issue_one(mb * 3 + nb, kt_load, slot);
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[p][nb], acc[mb][nb], 0, 0, 0);
+        }
+      if (DMA) {
+#pragma unroll
+        for (int i = NV * 3; i < LPW; ++i) issue_one(i, kt_load, slot);
+      }
+    };
+    bf16x8 ca[2], xa[2], cb[3][3], xb[3][3];
+    wait_stage(0, npro - 1);
+    block_barrier();
+    rd(0, 0, ca, cb);
+    int sk = 0;  // ring slot of stage kt
+    auto step = [&](int kt, auto more_tag, auto last_tag) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      const int sk1 = sk + 1 == NST ? 0 : sk + 1;
+      rd(sk, 1, xa, xb);
+      mm(ca, cb, std::false_type{}, 0, 0);
+      if (!LAST) {
+        wait_lds_reads();  // this wave's reads of stage kt done
+        const int newest = kt + NST - 1 < nk - 1 ? kt + NST - 1 : nk - 1;
+        wait_stage(kt + 1, newest);
+        block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again
+        rd(sk1, 0, ca, cb);
+      }
+      mm(xa, xb, more_tag, kt + NST, sk);  // stage kt+NST takes stage kt's slot
+      sk = sk1;
+    };
+    const int nmain = nk - NST > 0 ? nk - NST : 0;
+    for (int kt = 0; kt < nmain; ++kt) step(kt, std::true_type{}, std::false_type{});
+    for (int kt = nmain; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
+    step(nk - 1, std::false_type{}, std::true_type{});
+  };
+  switch (nvb) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 2>{}); break;
+  }
+
+  // 32x32 D layout: column lane & 31, rows 8*(r/4) + 4*(lane/32) + r%4
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    if (mb >= nvb) continue;
+#pragma unroll
+    for (int nb = 0; nb < 3; ++nb) {
+      const int e = e0 + (wn * 3 + nb) * 32 + l32;
+      if (e >= E) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (wm * 2 + mb) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < rows) logits[size_t(t0 + row) * E + e] = acc[mb][nb][r];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -303,10 +491,18 @@ hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const floa
     hipLaunchKernelGGL(router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
                        w_router, wsplit, n);
     const RouterSplit rs = router_split(s);
-    dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM, rs.splits);
-    hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(x), wsplit, rs.splits > 1 ? rpart : logits,
-                       s.T, s.d, E, rs.chunk);
+    float* dst = rs.splits > 1 ? rpart : logits;
+    if (router_pipelined(s)) {
+      const int n_et = (E + rp::BE - 1) / rp::BE;
+      const int units = ((s.T + rp::BM - 1) / rp::BM) * n_et * rs.splits;
+      hipLaunchKernelGGL(router_logits_pipe_kernel, dim3(unsigned((units + 7) / 8 * 8)), dim3(512), 0,
+                         st, static_cast<const bf16_t*>(x), wsplit, dst, s.T, s.d, E, rs.chunk,
+                         n_et, rs.splits, units);
+    } else {
+      dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM, rs.splits);
+      hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
+                         static_cast<const bf16_t*>(x), wsplit, dst, s.T, s.d, E, rs.chunk);
+    }
     if (rs.splits > 1) {
       const size_t nl = size_t(s.T) * E;
       hipLaunchKernelGGL(router_reduce_kernel, dim3(unsigned((nl + 1023) / 1024)), dim3(256), 0, st,

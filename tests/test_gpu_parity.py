@@ -134,6 +134,20 @@ def test_forward_full_size_sampled(name):
     check_forward(case, out, tokens=tokens)
 
 
+@pytest.mark.parametrize("T,d,N,Z,K", [(300, 160, 200, 13, 6), (513, 2048, 400, 200, 8),
+                                       (2300, 6144, 512, 256, 12)])
+def test_route_pipelined_ragged_split(T, d, N, Z, K):
+    """Router GEMM on 256-token x 192-expert tiles (d a multiple of 32): ragged token and
+    expert tiles, and K split into 5, 22 and 8 chunks whose partial logits are summed."""
+    lm = _lm()
+    wl = adhoc(name=f"adhoc_route_{T}_{d}", T=T, d=d, N=N, Z=Z, K=K,
+               expert_std=1.0 / np.sqrt(d), bias=("uniform", 0.5 / (N + Z)))
+    say(f"[route pipelined] T={T} d={d} E={N + Z}")
+    case = make_case(wl, ri=audited(wl), weights=False)
+    idx, gate = lm.route(case.x, case.w_router, case.bias, wl.K, wl.N)
+    check_route(case, idx, gate)
+
+
 # ---- invariants and edge cases on ad-hoc shapes (ragged tiles everywhere) --------------
 
 def run_adhoc(wl, ri=None, mutate=None):
