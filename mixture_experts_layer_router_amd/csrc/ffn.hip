@@ -426,23 +426,26 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
         }
       }
     };
-    // MFMAs of one substep; with DMA, this wave's loads of stage kt_load (into ring slot
-    // `slot`) go one per row block, the rest after the last block.
-    auto mm = [&](const bf16x8 (&a)[MB], const BFrag (&bq)[2], const float (&sc)[2], auto dma,
-                  int kt_load, int slot) {
-      constexpr bool DMA = decltype(dma)::value;
-      bf16x8 b[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if constexpr (FP8) {
-          if constexpr (NV > 0) {  // waves without rows skip it
-            const uint4 q = __builtin_bit_cast(uint4, bq[0]);
-            b[nb] = dequant8(nb == 0 ? make_uint2(q.x, q.y) : make_uint2(q.z, q.w), sc[nb]);
-          }
-        } else {
-          b[nb] = bq[nb];
-        }
+    // FP8: the two weight fragments of one substep as bf16 (codes times scales, exact).
+    // Each substep's fragments are converted one substep ahead, right after the MFMAs of
+    // the substep before were issued, so the conversions run beside those MFMAs instead of
+    // holding up the MFMAs that need them.
+    auto cvt = [&](const BFrag (&bq)[2], const float (&sc)[2], bf16x8 (&b)[2]) {
+      if constexpr (FP8 && NV > 0) {  // waves without rows skip it
+        const uint4 q = __builtin_bit_cast(uint4, bq[0]);
+        b[0] = dequant8(make_uint2(q.x, q.y), sc[0]);
+        b[1] = dequant8(make_uint2(q.z, q.w), sc[1]);
       }
+    };
+    // Keeps converted fragments where they are computed: without it the compiler sinks
+    // the conversions to their first use, past the barrier, back onto the MFMAs' path.
+    auto pin = [&](bf16x8 (&b)[2]) {
+      if constexpr (FP8 && NV > 0) asm volatile("" : "+v"(b[0]), "+v"(b[1]));
+    };
+    // MFMAs of one substep on bf16 weight fragments b; with DMA, this wave's loads of stage
+    // kt_load (into ring slot `slot`) go one per row block, the rest after the last block.
+    auto mm = [&](const bf16x8 (&a)[MB], const bf16x8 (&b)[2], auto dma, int kt_load, int slot) {
+      constexpr bool DMA = decltype(dma)::value;
 #pragma unroll
       for (int mb = 0; mb < NV; ++mb) {
         if (DMA && mb < IA + IB) issue_one(mb, kt_load, slot);
@@ -454,19 +457,28 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
         for (int i = NV; i < IA + IB; ++i) issue_one(i, kt_load, slot);
     };
     bf16x8 ca[MB], xa[MB];  // activation fragments of the current / next substep
-    BFrag cb[2], xb[2];     // weight fragments of the current / next substep
+    BFrag cb[2], xb[2];     // weight fragments of the current / next substep, as read
+    bf16x8 cw[2], xw[2];    // FP8: the same converted to bf16
     float sc[2] = {1.f, 1.f}, scn[2] = {1.f, 1.f};  // FP8 scales of stages kt / kt+1
     scales_of(0, sc);
     wait_stage(0, npro - 1);
     block_barrier();
     rd(0, 0, ca, cb);
+    cvt(cb, sc, cw);
     int sk = 0;  // ring slot of stage kt
     auto step = [&](int kt, auto more_tag, auto last_tag) {
       constexpr bool LAST = decltype(last_tag)::value;
       const int sk1 = sk + 1 == nst ? 0 : sk + 1;  // slot of stage kt+1
       if (!LAST) scales_of(kt + 1, scn);
       rd(sk, 1, xa, xb);
-      mm(ca, cb, sc, std::false_type{}, 0, 0);
+      if constexpr (FP8) {
+        mm(ca, cw, std::false_type{}, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // conversions after the MFMAs, before the wait
+        cvt(xb, sc, xw);
+        pin(xw);
+      } else {
+        mm(ca, cb, std::false_type{}, 0, 0);
+      }
       if (!LAST) {
         wait_lds_reads();  // this wave's reads of stage kt done
         const int newest = kt + nst - 1 < nk - 1 ? kt + nst - 1 : nk - 1;
@@ -474,7 +486,17 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
         block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again
         rd(sk1, 0, ca, cb);
       }
-      mm(xa, xb, sc, more_tag, kt + nst, sk);  // stage kt+nst takes stage kt's slot
+      // stage kt+nst takes stage kt's slot
+      if constexpr (FP8) {
+        mm(xa, xw, more_tag, kt + nst, sk);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!LAST) {
+          cvt(cb, scn, cw);
+          pin(cw);
+        }
+      } else {
+        mm(xa, xb, more_tag, kt + nst, sk);
+      }
       sk = sk1;
       if (!LAST) {
         sc[0] = scn[0];
