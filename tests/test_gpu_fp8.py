@@ -155,3 +155,31 @@ def test_forward_fp8_decode_full_size_sampled():
     err = rel_l2(y, ref["y"])
     say(f"  rel L2 {err:.2e}")
     assert err <= BF16_TOL
+
+
+def test_forward_fp8_prefill_full_size_sampled():
+    """The prefill layer at full size on FP8 weights, in the benchmark's launch
+    configuration: full 320-row tiles and the experts whose rows span two M-tiles.  The
+    oracle checks two tokens: one with the fewest FFN experts, and the token with the
+    fewest FFN experts among those routed to the most loaded expert (each oracle expert
+    costs seconds of CPU quantization)."""
+    import mixture_experts_layer_router_amd as lm
+    wl = configs.get("prefill")
+    say(f"fp8 forward full size: {wl.description}")
+    case = make_case(wl)
+    q = quantize_on_gpu(case.w)
+    out = lm.forward(case.x, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], wl.K, fp8=q)
+    idx = out["topk_idx"].cpu().numpy()
+    load = np.bincount(idx.ravel(), minlength=wl.E)[:wl.N]
+    top = int(np.argmax(load))
+    assert load[top] > 320, "expected an expert spanning two M-tiles"
+    ffn = (idx < wl.N).sum(1)
+    on_top = np.nonzero((idx == top).any(1))[0]
+    tokens = sorted({int(np.argmin(ffn)), int(on_top[np.argmin(ffn[on_top])])})
+    say(f"  sampled tokens {tokens} with {ffn[tokens].tolist()} FFN experts; expert {top} has {load[top]} rows")
+    ref = oracle_fp8_forward(case, tokens=tokens)
+    np.testing.assert_array_equal(idx[tokens], ref["idx"])
+    y = to_np(out["y"])[tokens]
+    err = rel_l2(y, ref["y"])
+    say(f"  rel L2 {err:.2e}")
+    assert err <= BF16_TOL

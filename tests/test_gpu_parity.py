@@ -135,10 +135,12 @@ def test_forward_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("T,d,N,Z,K", [(300, 160, 200, 13, 6), (513, 2048, 400, 200, 8),
-                                       (2300, 6144, 512, 256, 12)])
+                                       (2300, 6144, 512, 256, 12), (1, 64, 2, 0, 1),
+                                       (257, 32, 191, 2, 5)])
 def test_route_pipelined_ragged_split(T, d, N, Z, K):
     """Router GEMM on 256-token x 192-expert tiles (d a multiple of 32): ragged token and
-    expert tiles, and K split into 5, 22 and 8 chunks whose partial logits are summed."""
+    expert tiles, and K split into 5, 22, 8 and 2 chunks whose partial logits are summed;
+    a single token; a single 32-wide K step with a one-expert second expert tile."""
     lm = _lm()
     wl = adhoc(name=f"adhoc_route_{T}_{d}", T=T, d=d, N=N, Z=Z, K=K,
                expert_std=1.0 / np.sqrt(d), bias=("uniform", 0.5 / (N + Z)))
