@@ -459,19 +459,29 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
-// logits = sum of the split partials, added in split order (n = T*E, 4 per thread).
+// logits = sum of the split partials, added in split order (n = T*E, 4 per thread).  The
+// partials are loaded eight splits at a time before they are added, so each thread keeps
+// eight loads in flight (a few-token layer has few threads and up to 64 splits).
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ rpart,
                                                             float* __restrict__ logits,
                                                             int splits, size_t n) {
   const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (n % 4 == 0 && i + 3 < n) {  // every partial array starts 16-byte aligned
     float4 a = *reinterpret_cast<const float4*>(rpart + i);
-    for (int sp = 1; sp < splits; ++sp) {
-      const float4 b = *reinterpret_cast<const float4*>(rpart + sp * n + i);
-      a.x += b.x;
-      a.y += b.y;
-      a.z += b.z;
-      a.w += b.w;
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+      float4 b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < splits) b[j] = *reinterpret_cast<const float4*>(rpart + (s0 + j) * n + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (s0 + j < splits) {
+          a.x += b[j].x;
+          a.y += b[j].y;
+          a.z += b[j].z;
+          a.w += b[j].w;
+        }
+      }
     }
     *reinterpret_cast<float4*>(logits + i) = a;
   } else {
