@@ -17,6 +17,12 @@
 #include "common.h"
 #include "lds_dma.h"
 
+// Wavefront reductions of the ROCm device library (ockl): DPP steps in a fixed order, the
+// result in every active lane.
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
+extern "C" __device__ __attribute__((const)) int __ockl_wfred_min_i32(int);
+
 namespace lcm {
 
 // ---------------------------------------------------------------------------------------
@@ -405,8 +411,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     v[j] = e < E ? row[e] : -INFINITY;
     m = fmaxf(m, v[j]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // wavefront reductions (DPP, fixed order; every lane gets the same result)
+  m = __ockl_wfred_max_f32(m);
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -414,9 +420,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     v[j] = e < E ? expf(v[j] - m) : 0.f;
     sum += v[j];
   }
-  // butterfly: a + b == b + a exactly, so every lane ends with the same bits
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  sum = __ockl_wfred_add_f32(sum);
   float s[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -424,36 +428,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     v[j] = v[j] / sum;  // p, IEEE division
     s[j] = e < E ? v[j] + bias[e] : -INFINITY;
   }
-  uint64_t taken = 0;
+  // K rounds: the largest s left wins, the lowest expert index among equal s.  Each round
+  // takes the lane's best remaining slot (ascending slots keep the lower index), the
+  // wavefront maximum of those, then the lowest expert index holding that maximum.
   for (int k = 0; k < K; ++k) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      const bool ok = !((taken >> j) & 1ull) && e < E;
-      if (ok && (s[j] > bv || be == 0x7fffffff)) {  // ascending j: first max keeps lower e
+      if (e < E && s[j] != -INFINITY && (s[j] > bv || be == 0x7fffffff)) {
         bv = s[j];
         be = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) {
-      const int j = be >> 6;
+    const float wm = __ockl_wfred_max_f32(bv);
+    const int we = __ockl_wfred_min_i32(bv == wm ? be : 0x7fffffff);
+    if ((we & 63) == lane) {
+      const int j = we >> 6;
       float p = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < EPL; ++jj)
-        if (jj == j) p = v[jj];
-      taken |= 1ull << j;
-      idx[size_t(t) * K + k] = be;
+      for (int jj = 0; jj < EPL; ++jj) {
+        if (jj == j) {
+          p = v[jj];
+          s[jj] = -INFINITY;  // taken
+        }
+      }
+      idx[size_t(t) * K + k] = we;
       gate[size_t(t) * K + k] = p;
     }
   }
