@@ -20,7 +20,10 @@ beside it.  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZ
 decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
 (gate/up + down) is bound by streaming the weights of the experts that received at least
 one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
-graph and replayed (graph_ms_per_step), and run on block-FP8 expert weights (fp8_*).
+graph and replayed (graph_ms_per_step), run on packed bf16 expert weights (packed_*), and
+run on block-FP8 expert weights (fp8_*).
+prefill_packed: the prefill layer on packed bf16 expert weights (lc_moe_pack_weights; the
+same bits as the row-major weights).
 prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
 overlap: a dense SwiGLU FFN (width 2d) over the same tokens beside the layer, serial on one
 stream against concurrent on two streams.
@@ -102,6 +105,21 @@ def use_fp8(lm, st):
     st["fp8"] = lm.quantize_weights(st["w"]["gate"], st["w"]["up"], st["w"]["down"])
     st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"], st["fp8"])
     torch.cuda.synchronize()
+
+
+def use_packed(lm, st):
+    """Re-lay the layer's bf16 expert weights in the packed tile layout and point the
+    forward at them (the same values; the layer computes the same bits)."""
+    import torch
+    st["packed"] = lm.pack_weights(st["w"]["gate"], st["w"]["up"], st["w"]["down"])
+    st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"], None,
+                            st["packed"])
+    torch.cuda.synchronize()
+
+
+def drop_packed(lm, st):
+    st.pop("packed", None)
+    st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"])
 
 
 def run_steps(lm, st, steps, warmup):
@@ -293,12 +311,19 @@ def decode_runs(lm, dev, steps, warmup):
             ffn_ms = float(np.mean(stages["gate_up"]) + np.mean(stages["down"]))
             gbs = wbytes / (ffn_ms * 1e-3) / 1e9
             gms = graph_ms(lm, st, steps)
+            use_packed(lm, st)
+            totalp, stagesp = run_steps(lm, st, steps, warmup)
+            ffnp = float(np.mean(stagesp["gate_up"]) + np.mean(stagesp["down"]))
+            gbsp = wbytes / (ffnp * 1e-3) / 1e9
+            drop_packed(lm, st)
             use_fp8(lm, st)
             total8, stages8 = run_steps(lm, st, steps, warmup)
             ffn8 = float(np.mean(stages8["gate_up"]) + np.mean(stages8["down"]))
             gbs8 = wbytes / 2 / (ffn8 * 1e-3) / 1e9  # FP8 codes: half the bytes (scales < 0.02%)
             res.append({"T": T, "zero_share_pct": share, "ms_per_step": total / steps,
-                        "graph_ms_per_step": gms, "fp8_ms_per_step": total8 / steps, "fp8_ffn_ms": ffn8,
+                        "graph_ms_per_step": gms, "packed_ms_per_step": totalp / steps, "packed_ffn_ms": ffnp,
+                        "packed_ffn_weight_GBps": gbsp, "packed_hbm_frac": gbsp / HBM_PEAK_GBS,
+                        "fp8_ms_per_step": total8 / steps, "fp8_ffn_ms": ffn8,
                         "fp8_ffn_weight_GBps": gbs8, "fp8_hbm_frac": gbs8 / HBM_PEAK_GBS,
                         "tokens_per_s": T * steps / (total * 1e-3), "touched_experts": touched,
                         "ffn_rows": int(load[:wl.N].sum()), "ffn_ms": ffn_ms,
@@ -306,6 +331,7 @@ def decode_runs(lm, dev, steps, warmup):
                         "stages_ms": {k: float(np.mean(v)) for k, v in stages.items()}})
             log(f"decode T={T} share={share}%: {total / steps:.3f} ms/step ({gms:.3f} from a graph), "
                 f"FFN {ffn_ms:.3f} ms, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak); "
+                f"packed weights FFN {ffnp:.3f} ms, {gbsp:.0f} GB/s ({gbsp / HBM_PEAK_GBS:.1%}); "
                 f"FP8 weights {total8 / steps:.3f} ms/step, FFN {ffn8:.3f} ms, {gbs8:.0f} GB/s "
                 f"({gbs8 / HBM_PEAK_GBS:.1%})")
             del st
@@ -386,6 +412,17 @@ def main():
                 "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
         "stages_ms": st_ms,
     }
+    use_packed(lm, st)
+    totalp, stagesp = run_steps(lm, st, args.steps, args.warmup)
+    stp = {k: float(np.mean(v)) for k, v in stagesp.items()}
+    result["prefill_packed"] = {"ms_per_step": totalp / args.steps,
+                                "tokens_per_s": wl.T * args.steps / (totalp * 1e-3), "stages_ms": stp,
+                                "gate_up_GBps": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9,
+                                "gate_up_frac": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    log(f"packed weights: {totalp / args.steps:.3f} ms/step; stages "
+        f"{json.dumps({k: round(v, 4) for k, v in stp.items()})}")
+    drop_packed(lm, st)
+    torch.cuda.empty_cache()
     use_fp8(lm, st)
     total8, stages8 = run_steps(lm, st, args.steps, args.warmup)
     st8 = {k: float(np.mean(v)) for k, v in stages8.items()}

@@ -75,6 +75,11 @@ typedef struct {
   const void* fp8;       /* NULL, or the block-FP8 expert weights made by
                             lc_moe_quantize_weights; then the FFN uses them and w_gate,
                             w_up, w_down are not read (they may be NULL)                 */
+  const void* packed;    /* NULL, or the bf16 expert weights re-laid by
+                            lc_moe_pack_weights; then the FFN reads them instead of
+                            w_gate, w_up, w_down (which may be NULL) and computes the same
+                            bits.  At most one of fp8 and packed may be set (else
+                            LC_MOE_E_DTYPE)                                              */
 } lc_moe_weights;
 
 /* Stages of lc_moe_forward, in launch order (names from lc_moe_stage_name). */
@@ -173,6 +178,25 @@ size_t lc_moe_fp8_weights_size(const lc_moe_shape* shape);
 lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_gate,
                                       const void* w_up, const void* w_down, void* fp8_weights,
                                       size_t fp8_weights_bytes, hipStream_t stream);
+
+/* Packed bf16 expert weights: the same values as W_gate, W_up [N][I][d] and W_down
+ * [N][d][I], re-laid so that every (expert, 128 gate/up or 256 down output columns, 32-wide
+ * K step) tile is one contiguous 16 KB block in the order the FFN kernel stages it.  A
+ * one-time copy, made when the weights are loaded; the layer computed with it is the same
+ * to the bit as with the row-major weights, and reading contiguous blocks streams the
+ * weights faster.  For callers that do this once at load time.
+ * lc_moe_packed_weights_size: bytes of the packed form for this shape (about the size of
+ * the three expert matrices); 0 when the shape has none (fp32 layers, d or I not a
+ * multiple of 32).
+ * lc_moe_pack_weights: writes it into packed_weights (packed_weights_bytes >=
+ * lc_moe_packed_weights_size, 16-byte aligned); pass that as lc_moe_weights.packed.  Needs
+ * dtype LC_MOE_BF16 (else LC_MOE_E_DTYPE) and a shape with a packed form (else
+ * LC_MOE_E_SHAPE); a short buffer gives LC_MOE_E_WORKSPACE.  Enqueued on `stream`; the
+ * source weights must stay valid until it has run. */
+size_t lc_moe_packed_weights_size(const lc_moe_shape* shape);
+lc_moe_status lc_moe_pack_weights(const lc_moe_shape* shape, const void* w_gate,
+                                  const void* w_up, const void* w_down, void* packed_weights,
+                                  size_t packed_weights_bytes, hipStream_t stream);
 
 /* PID gains of the expert-bias controller (host struct). */
 typedef struct {

@@ -8,10 +8,10 @@ device memory and streams.  The library is opened on first use and a missing bui
 
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
 ``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_bias_update``,
-``lc_moe_quantize_weights``, ``lc_moe_fp8_weights_size``, ``lc_moe_workspace_size``);
-``route``, ``expert_load``, ``permute``, ``forward``, ``bias_update`` and
-``quantize_weights`` allocate outputs and a workspace with torch where needed and call
-them.
+``lc_moe_quantize_weights``, ``lc_moe_fp8_weights_size``, ``lc_moe_pack_weights``,
+``lc_moe_packed_weights_size``, ``lc_moe_workspace_size``); ``route``, ``expert_load``,
+``permute``, ``forward``, ``bias_update``, ``quantize_weights`` and ``pack_weights``
+allocate outputs and a workspace with torch where needed and call them.
 """
 from __future__ import annotations
 
@@ -41,7 +41,7 @@ class Shape(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("fp8", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("fp8", ctypes.c_void_p), ("packed", ctypes.c_void_p)]
 
 
 class Pid(ctypes.Structure):
@@ -61,6 +61,8 @@ _SIG = {
                                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "lc_moe_fp8_weights_size": (_sz, [ctypes.POINTER(Shape)]),
     "lc_moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lc_moe_packed_weights_size": (_sz, [ctypes.POINTER(Shape)]),
+    "lc_moe_pack_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_bias_update": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Pid), _vp, _vp,
                                           _vp, _vp, _vp, _vp]),
     "lc_moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -155,9 +157,9 @@ def lc_moe_permute(shape, x, topk_idx, ffn_offsets, perm_token, slot_row, x_perm
            "lc_moe_permute")
 
 
-def _weights(w_router, bias, w_gate, w_up, w_down, fp8=None) -> Weights:
+def _weights(w_router, bias, w_gate, w_up, w_down, fp8=None, packed=None) -> Weights:
     p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    return Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8))
+    return Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8), p(packed))
 
 
 def lc_moe_fp8_weights_size(shape: Shape) -> int:
@@ -168,6 +170,16 @@ def lc_moe_quantize_weights(shape, w_gate, w_up, w_down, fp8_weights, stream=Non
     _check(lib().lc_moe_quantize_weights(ctypes.byref(shape), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                         _ptr(fp8_weights), _nbytes(fp8_weights), _stream(stream)),
            "lc_moe_quantize_weights")
+
+
+def lc_moe_packed_weights_size(shape: Shape) -> int:
+    return int(lib().lc_moe_packed_weights_size(ctypes.byref(shape)))
+
+
+def lc_moe_pack_weights(shape, w_gate, w_up, w_down, packed_weights, stream=None):
+    _check(lib().lc_moe_pack_weights(ctypes.byref(shape), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                    _ptr(packed_weights), _nbytes(packed_weights), _stream(stream)),
+           "lc_moe_pack_weights")
 
 
 def lc_moe_forward(shape, x, weights: Weights, y, topk_idx, topk_gate, load, workspace,
@@ -251,9 +263,11 @@ def permute(x, topk_idx, N, E, with_x_perm=True, workspace=None):
     return out
 
 
-def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_events=None, fp8=None):
+def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_events=None, fp8=None,
+            packed=None):
     """dict(y, topk_idx, topk_gate, load); x [T,d]; w_gate/w_up [N,I,d]; w_down [N,d,I];
-    fp8: optional block-FP8 weights from quantize_weights (then used instead)."""
+    fp8: optional block-FP8 weights from quantize_weights (then used instead);
+    packed: optional packed bf16 weights from pack_weights (then read instead)."""
     import torch
     N, I, _ = w_gate.shape
     E = w_router.shape[0]
@@ -264,7 +278,7 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_ev
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     gate = torch.empty((T, K), dtype=torch.float32, device=dev)
     load = torch.empty(E, dtype=torch.int32, device=dev)
-    wts = _weights(w_router, bias, w_gate, w_up, w_down, fp8)
+    wts = _weights(w_router, bias, w_gate, w_up, w_down, fp8, packed)
     if stage_events is None:
         lc_moe_forward(shape, x, wts, y, idx, gate, load, ws)
     else:
@@ -291,4 +305,18 @@ def quantize_weights(w_gate, w_up, w_down):
         raise LcMoeError(2, "lc_moe_fp8_weights_size")
     out = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
     lc_moe_quantize_weights(shape, w_gate, w_up, w_down, out)
+    return out
+
+
+def pack_weights(w_gate, w_up, w_down):
+    """Packed form of bf16 expert weights (W_gate, W_up [N,I,d], W_down [N,d,I]) as a uint8
+    device tensor, for ``forward(..., packed=...)`` / ``Weights.packed``."""
+    import torch
+    N, I, d = w_gate.shape
+    shape = make_shape(1, d, N, 0, 1, I, BF16)
+    n = lc_moe_packed_weights_size(shape)
+    if n == 0:
+        raise LcMoeError(2, "lc_moe_packed_weights_size")
+    out = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
+    lc_moe_pack_weights(shape, w_gate, w_up, w_down, out)
     return out

@@ -155,10 +155,15 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   LCM_CHECK(check_ptr(x));
   LCM_CHECK(check_ptr(weights->w_router));
   LCM_CHECK(check_ptr(weights->bias));
+  if (weights->fp8 && weights->packed) return LC_MOE_E_DTYPE;  // one weight format
   if (weights->fp8) {
     LCM_CHECK(check_ptr(weights->fp8));
     if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
     if (plan_fp8(*shape).total == 0) return LC_MOE_E_SHAPE;
+  } else if (weights->packed) {
+    LCM_CHECK(check_ptr(weights->packed));
+    if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
+    if (plan_packed(*shape).total == 0) return LC_MOE_E_SHAPE;
   } else {
     LCM_CHECK(check_ptr(weights->w_gate));
     LCM_CHECK(check_ptr(weights->w_up));
@@ -197,10 +202,11 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   if (!mark(1)) return LC_MOE_E_DEVICE;
   LCM_CHECK(permute_core(s, idx, p, workspace, ld, offsets, slot_row, perm_token, nullptr, stream));
   if (!mark(2)) return LC_MOE_E_DEVICE;
-  LCM_LAUNCH(launch_ffn_gate_up(s, x, perm_token, weights->w_gate, weights->w_up, weights->fp8, hbuf,
-                                mtiles, offsets, n_mtiles, p.mt_max, stream));
+  LCM_LAUNCH(launch_ffn_gate_up(s, x, perm_token, weights->w_gate, weights->w_up, weights->fp8,
+                                weights->packed, hbuf, mtiles, offsets, n_mtiles, p.mt_max, stream));
   if (!mark(3)) return LC_MOE_E_DEVICE;
-  LCM_LAUNCH(launch_ffn_down(s, hbuf, weights->w_down, weights->fp8, ybuf, mtiles, offsets, n_mtiles,
+  LCM_LAUNCH(launch_ffn_down(s, hbuf, weights->w_down, weights->fp8, weights->packed, ybuf, mtiles,
+                             offsets, n_mtiles,
                              p.mt_max, stream));
   if (!mark(4)) return LC_MOE_E_DEVICE;
   LCM_LAUNCH(launch_combine(s, x, ybuf, slot_row, gate, y, stream));
@@ -225,6 +231,26 @@ lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_g
   LCM_CHECK(check_ptr(fp8_weights));
   if (fp8_weights_bytes < plan_fp8(*shape).total) return LC_MOE_E_WORKSPACE;
   LCM_LAUNCH(launch_quantize_weights(*shape, w_gate, w_up, w_down, fp8_weights, stream));
+  return LC_MOE_OK;
+}
+
+size_t lc_moe_packed_weights_size(const lc_moe_shape* shape) {
+  if (check_shape(shape) != LC_MOE_OK || shape->dtype != LC_MOE_BF16) return 0;
+  return plan_packed(*shape).total;
+}
+
+lc_moe_status lc_moe_pack_weights(const lc_moe_shape* shape, const void* w_gate,
+                                  const void* w_up, const void* w_down, void* packed_weights,
+                                  size_t packed_weights_bytes, hipStream_t stream) {
+  LCM_CHECK(check_shape(shape));
+  if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
+  if (plan_packed(*shape).total == 0) return LC_MOE_E_SHAPE;
+  LCM_CHECK(check_ptr(w_gate));
+  LCM_CHECK(check_ptr(w_up));
+  LCM_CHECK(check_ptr(w_down));
+  LCM_CHECK(check_ptr(packed_weights));
+  if (packed_weights_bytes < plan_packed(*shape).total) return LC_MOE_E_WORKSPACE;
+  LCM_LAUNCH(launch_pack_weights(*shape, w_gate, w_up, w_down, packed_weights, stream));
   return LC_MOE_OK;
 }
 

@@ -171,6 +171,27 @@ inline Fp8Plan plan_fp8(const lc_moe_shape& s) {
   return p;
 }
 
+// bf16 expert weights packed for the pipelined FFN kernel (lc_moe_pack_weights).  Regions
+// (256-byte aligned, in this order):
+//   gu [N][ceil(I/128)][d/32][256 rows][64 B]  rows 0..127 of n-tile nt are W_gate rows
+//      nt*128 + r, rows 128..255 the W_up rows nt*128 + r - 128 (rows past I are zero)
+//   d  [N][ceil(d/256)][I/32][256 rows][64 B]  row r of n-tile nt is W_down row nt*256 + r
+//      (rows past d are zero)
+// A row holds the 32 columns of one K step as four 16-byte chunks, chunk c in slot
+// c ^ swz4(r): each 16 KB block is exactly the LDS image of one stage's weight rows.
+struct PackPlan {
+  size_t gu, d, total;
+};
+inline PackPlan plan_packed(const lc_moe_shape& s) {
+  PackPlan p{};
+  if (!ffn_pipelined(s)) return p;
+  const size_t N = s.N;
+  p.gu = 0;
+  p.d = align256(N * size_t((s.I + 127) / 128) * size_t(s.d / 32) * 16384);
+  p.total = p.d + N * size_t((s.d + 255) / 256) * size_t(s.I / 32) * 16384;
+  return p;
+}
+
 // ---- launchers (host functions defined in the .hip files) ------------------------------
 
 // Router logits L[T][E] = x W_r^T (fp32 result).  bf16 layers: W_r is first split into
@@ -203,14 +224,20 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s
 // Grouped SwiGLU FFN over the FFN picks.
 // With fp8 != nullptr (packed block-FP8 weights, pipelined shapes only) the weights come
 // from it and w_gate / w_up / w_down are not read.
+// With packed != nullptr (lc_moe_pack_weights, pipelined shapes only) the bf16 weights
+// come from it instead.
 hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
-                              const void* w_gate, const void* w_up, const void* fp8, void* hbuf,
-                              const MTile* mtiles, const int32_t* offsets,
-                              const int32_t* n_mtiles, int mt_max, hipStream_t st);
+                              const void* w_gate, const void* w_up, const void* fp8,
+                              const void* packed, void* hbuf, const MTile* mtiles,
+                              const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
+                              hipStream_t st);
 hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
-                           const void* fp8, void* ybuf, const MTile* mtiles,
+                           const void* fp8, const void* packed, void* ybuf, const MTile* mtiles,
                            const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
                            hipStream_t st);
+// bf16 expert weights -> the packed layout of plan_packed.
+hipError_t launch_pack_weights(const lc_moe_shape& s, const void* w_gate, const void* w_up,
+                               const void* w_down, void* packed, hipStream_t st);
 // Quantize bf16 W_gate, W_up [N][I][d] and W_down [N][d][I] into the packed block-FP8
 // form (plan_fp8) at `out`.
 hipError_t launch_quantize_weights(const lc_moe_shape& s, const void* w_gate, const void* w_up,

@@ -242,8 +242,10 @@ __device__ __forceinline__ bf16x8 dequant8(uint2 q, float scale) {
   return r;
 }
 
-// FP8 = false: weights bf16 row-major (w0, w1).  FP8 = true: weights are the packed
-// block-FP8 codes (qcodes: this matrix pair's region, one 8 KB tile block per stage) with
+// FP8 = false: weights bf16, row-major (w0, w1) or, with bpacked, packed by
+// lc_moe_pack_weights (w0: this matrix pair's region; stage kt of a unit is one 16 KB block
+// holding exactly the LDS image of the stage's 256 weight rows).  FP8 = true: weights are
+// the packed block-FP8 codes (qcodes: this matrix pair's region, one 8 KB tile block per stage) with
 // fp32 power-of-two scales (qscales; nrb_rows row blocks x nkb column blocks per matrix);
 // each weight fragment is converted to bf16 (v_cvt_scalef32_pk_bf16_fp8, exact) right
 // before its MFMAs, so the MFMAs see exactly the dequantized weights.
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     const unsigned char* __restrict__ qcodes, const float* __restrict__ qscales, int nrb_rows,
     int nkb, bf16_t* __restrict__ out, const MTile* __restrict__ mtiles,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_mtiles_ptr, int kdim,
-    int ncols, int n_ntiles) {
+    int ncols, int n_ntiles, int bpacked) {
   constexpr int BM = kBmPipe;             // 320
   constexpr int BK = 32;                  // K step
   constexpr int LDS_BYTES = 160 * 1024;   // the ring
@@ -302,6 +304,12 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   if (FP8) {
     srcQ = reinterpret_cast<const bf16_t*>(qcodes + (size_t(e) * n_ntiles + ntile) * (kdim / BK) * size_t(8192) +
                                            wave * 1024 + lane * 16);
+  } else if (bpacked) {
+    // packed bf16: weight load q is the 1 KB piece q of the stage's 16 KB block
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+      srcB[i] = w0 + (size_t(e) * n_ntiles + ntile) * (kdim / BK) * size_t(8192) + (wave + 8 * i) * 512 +
+                lane * 8;
   } else {
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
@@ -330,6 +338,9 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   const int krot = (j * 7 + ntile * 3) % nk;
 #endif
   auto kphys = [&](int kt) { const int k = kt + krot; return (k >= nk ? k - nk : k) * BK; };
+  // source elements per K element of the weight loads: 1 row-major, 256 packed (one 8192-
+  // element block per 32-wide K step)
+  const int bmul = bpacked ? 256 : 1;
   // Ring geometry from the tile's rows: a stage holds the activation rows the MFMAs read
   // (rows rounded up to 32) and the 256 weight rows, and the ring has as many stages as
   // fit in 160 KB, up to 16 (bf16 weights: 4 at 320 rows, 5 at 256, 8 for decode-sized
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     } else if (FP8) {
       dma16(srcQ + size_t(kphys(kt)) * 128, st + a_bytes + wave * 1024);  // 8 KB per stage
     } else {
-      dma16(srcB[i - IA] + kphys(kt), st + a_bytes + (wave + 8 * (i - IA)) * 1024);
+      dma16(srcB[i - IA] + kphys(kt) * bmul, st + a_bytes + (wave + 8 * (i - IA)) * 1024);
     }
   };
   // wait until this wave's loads of stage s landed, `newest` being the last stage issued
@@ -550,7 +561,7 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
       const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,    \
       const bf16_t* __restrict__, const unsigned char* __restrict__, const float* __restrict__, \
       int, int, bf16_t* __restrict__, const MTile* __restrict__, const int32_t* __restrict__, \
-      const int32_t* __restrict__, int, int, int);
+      const int32_t* __restrict__, int, int, int, int);
 LCM_INST(0, false)
 LCM_INST(1, false)
 LCM_INST(0, true)
@@ -619,9 +630,10 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
 }
 
 hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
-                              const void* w_gate, const void* w_up, const void* fp8, void* hbuf,
-                              const MTile* mtiles, const int32_t* offsets,
-                              const int32_t* n_mtiles, int mt_max, hipStream_t st) {
+                              const void* w_gate, const void* w_up, const void* fp8,
+                              const void* packed, void* hbuf, const MTile* mtiles,
+                              const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
+                              hipStream_t st) {
   if (s.dtype == LC_MOE_BF16 && ffn_pipelined(s)) {
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
@@ -632,12 +644,18 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
       ffn_bf16_pipe_kernel<0, true><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, nullptr, nullptr, qb + q.codes_gu,
           reinterpret_cast<const float*>(qb + q.scales_gu), q.nrb_i, q.nrb_d,
-          static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn);
+          static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
+    else if (packed)
+      ffn_bf16_pipe_kernel<0, false><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(x), perm_token,
+          reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).gu),
+          nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
+          s.I, nn, 1);
     else
       ffn_bf16_pipe_kernel<0, false><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
           static_cast<const bf16_t*>(w_up), nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf),
-          mtiles, offsets, n_mtiles, s.d, s.I, nn);
+          mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
@@ -659,7 +677,7 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
 }
 
 hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
-                           const void* fp8, void* ybuf, const MTile* mtiles,
+                           const void* fp8, const void* packed, void* ybuf, const MTile* mtiles,
                            const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
                            hipStream_t st) {
   if (s.dtype == LC_MOE_BF16 && ffn_pipelined(s)) {
@@ -672,12 +690,18 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
       ffn_bf16_pipe_kernel<1, true><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, nullptr, nullptr, qb + q.codes_d,
           reinterpret_cast<const float*>(qb + q.scales_d), q.nrb_d, q.nrb_i,
-          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn);
+          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn, 0);
+    else if (packed)
+      ffn_bf16_pipe_kernel<1, false><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(hbuf), nullptr,
+          reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).d),
+          nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I,
+          s.d, nn, 1);
     else
       ffn_bf16_pipe_kernel<1, false><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
           nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d,
-          nn);
+          nn, 0);
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.d + 255) / 256;
     const size_t units = size_t(mt_max) * nn;

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -126,3 +126,42 @@ def test_fp8_size_and_quantize_validation():
     assert f(ctypes.byref(s), None, P, P, P, n, None) == 1
     assert f(ctypes.byref(s), P, P, MIS, P, n, None) == 4
     assert f(ctypes.byref(s), P, P, P, P, n - 1, None) == 5
+
+
+def test_packed_size_and_pack_validation():
+    s = lm.make_shape(T=64, d=128, N=8, Z=4, K=2, I=256, dtype=lm.BF16)
+    n = lm.lc_moe_packed_weights_size(s)
+    # gate/up: 2 n-tiles x 4 K steps x 16 KB; down: 1 n-tile x 8 K steps x 16 KB, per expert
+    assert n == 8 * (2 * 4 + 1 * 8) * 16384
+    assert lm.lc_moe_packed_weights_size(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)) == 0
+    assert lm.lc_moe_packed_weights_size(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)) == 0  # d % 32
+    # ragged n-tiles are zero-padded to whole blocks: I=160 -> 2 gate/up n-tiles of 9 K steps,
+    # d=288 -> 2 down n-tiles of 5 K steps, 3 experts
+    assert lm.lc_moe_packed_weights_size(lm.make_shape(1, 288, 3, 0, 1, 160, lm.BF16)) == \
+        3 * (2 * 9 + 2 * 5) * 16384
+    f = lm.lib().lc_moe_pack_weights
+    assert f(ctypes.byref(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)), P, P, P, P, n, None) == 3
+    assert f(ctypes.byref(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)), P, P, P, P, n, None) == 2
+    assert f(ctypes.byref(s), None, P, P, P, n, None) == 1
+    assert f(ctypes.byref(s), P, P, MIS, P, n, None) == 4
+    assert f(ctypes.byref(s), P, P, P, P, n - 1, None) == 5
+
+
+def test_forward_weight_format_validation():
+    """fp8 and packed weights are exclusive, and each needs a bf16 shape that has that form;
+    all of it is decided on the host before anything is enqueued."""
+    L = lm.lib()
+    sp = ctypes.byref(good_shape())
+    nb = lm.lc_moe_workspace_size(good_shape())
+    both = lm.Weights(P, P, None, None, None, P, P)
+    assert L.lc_moe_forward(sp, P, ctypes.byref(both), P, None, None, None, P, nb, None) == 3
+    packed = lm.Weights(P, P, None, None, None, None, P)
+    f32 = lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)
+    assert L.lc_moe_forward(ctypes.byref(f32), P, ctypes.byref(packed), P, None, None, None, P,
+                            lm.lc_moe_workspace_size(f32), None) == 3
+    odd = lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)
+    assert L.lc_moe_forward(ctypes.byref(odd), P, ctypes.byref(packed), P, None, None, None, P,
+                            lm.lc_moe_workspace_size(odd), None) == 2
+    mis = lm.Weights(P, P, None, None, None, None, MIS)
+    assert L.lc_moe_forward(sp, P, ctypes.byref(mis), P, None, None, None, P, nb, None) == 4
+
