@@ -247,8 +247,8 @@ __device__ __forceinline__ bf16x8 dequant8(uint2 q, float scale) {
 // holding exactly the LDS image of the stage's 256 weight rows).  FP8 = true: weights are
 // the packed block-FP8 codes (qcodes: this matrix pair's region, one 8 KB tile block per stage) with
 // fp32 power-of-two scales (qscales; nrb_rows row blocks x nkb column blocks per matrix);
-// each weight fragment is converted to bf16 (v_cvt_scalef32_pk_bf16_fp8, exact) right
-// before its MFMAs, so the MFMAs see exactly the dequantized weights.
+// each weight fragment is converted to bf16 (v_cvt_scalef32_pk_bf16_fp8, exact) one
+// substep before its MFMAs, so the MFMAs see exactly the dequantized weights.
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     const bf16_t* __restrict__ a_src, const int32_t* __restrict__ perm_token,
@@ -329,14 +329,10 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   }
   const int per_stage = na + IB;  // this wave's loads per stage (vmcnt increments)
   const int nk = kdim / BK;
-#ifdef LCM_NO_KROT
-  const int krot = 0;
-#else
   // Each work unit starts its K loop at its own offset: rows of one tile share their low
   // address bits (row strides are multiples of 4 KB), so tiles running side by side are
   // spread over the memory channels.
   const int krot = (j * 7 + ntile * 3) % nk;
-#endif
   auto kphys = [&](int kt) { const int k = kt + krot; return (k >= nk ? k - nk : k) * BK; };
   // source elements per K element of the weight loads: 1 row-major, 256 packed (one 8192-
   // element block per 32-wide K step)
