@@ -347,6 +347,9 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the packed-weight runs (they launch the same kernel names as the "
+                         "row-major runs, which a per-kernel profile would then mix)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the dense-FFN-beside-the-layer two-stream measurement")
     ap.add_argument("--calib-copy", action="store_true",
@@ -412,17 +415,18 @@ def main():
                 "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
         "stages_ms": st_ms,
     }
-    use_packed(lm, st)
-    totalp, stagesp = run_steps(lm, st, args.steps, args.warmup)
-    stp = {k: float(np.mean(v)) for k, v in stagesp.items()}
-    result["prefill_packed"] = {"ms_per_step": totalp / args.steps,
-                                "tokens_per_s": wl.T * args.steps / (totalp * 1e-3), "stages_ms": stp,
-                                "gate_up_GBps": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9,
-                                "gate_up_frac": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    log(f"packed weights: {totalp / args.steps:.3f} ms/step; stages "
-        f"{json.dumps({k: round(v, 4) for k, v in stp.items()})}")
-    drop_packed(lm, st)
-    torch.cuda.empty_cache()
+    if not args.no_packed:
+        use_packed(lm, st)
+        totalp, stagesp = run_steps(lm, st, args.steps, args.warmup)
+        stp = {k: float(np.mean(v)) for k, v in stagesp.items()}
+        result["prefill_packed"] = {"ms_per_step": totalp / args.steps,
+                                    "tokens_per_s": wl.T * args.steps / (totalp * 1e-3), "stages_ms": stp,
+                                    "gate_up_GBps": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9,
+                                    "gate_up_frac": gu_bytes / (stp["gate_up"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"packed weights: {totalp / args.steps:.3f} ms/step; stages "
+            f"{json.dumps({k: round(v, 4) for k, v in stp.items()})}")
+        drop_packed(lm, st)
+        torch.cuda.empty_cache()
     use_fp8(lm, st)
     total8, stages8 = run_steps(lm, st, args.steps, args.warmup)
     st8 = {k: float(np.mean(v)) for k, v in stages8.items()}
