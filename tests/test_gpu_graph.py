@@ -11,17 +11,28 @@ from tests.gpu_common import BF16_TOL, F32_TOL, adhoc, audited, make_case, oracl
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,T,d,I", [("bf16", 64, 512, 256), ("bf16", 200, 256, 96), ("f32", 48, 128, 64)])
-def test_forward_graph_replay(dtype, T, d, I):
+@pytest.mark.parametrize("dtype,T,d,I,wfmt", [("bf16", 64, 512, 256, "rows"), ("bf16", 200, 256, 96, "rows"),
+                                              ("f32", 48, 128, 64, "rows"), ("bf16", 64, 512, 256, "packed"),
+                                              ("bf16", 200, 256, 96, "fp8")])
+def test_forward_graph_replay(dtype, T, d, I, wfmt):
+    """wfmt: row-major bf16/fp32 weights, packed bf16 weights, or block-FP8 weights."""
     import torch
     import mixture_experts_layer_router_amd as lm
-    wl = adhoc(name=f"graph_{dtype}_{T}", T=T, d=d, N=24, Z=12, K=6, I=I, dtype=dtype, seed_key=(300, T),
+    wl = adhoc(name=f"graph_{dtype}_{T}_{wfmt}", T=T, d=d, N=24, Z=12, K=6, I=I, dtype=dtype, seed_key=(300, T),
                expert_std=1.0 / np.sqrt(d))
     say(f"graph replay {wl.name}")
     case = make_case(wl, ri=audited(wl))
     shape = lm.make_shape(wl.T, wl.d, wl.N, wl.Z, wl.K, wl.I, case.x.dtype)
     ws = lm.workspace_for(shape, case.x.device)
-    wts = lm._weights(case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"])
+    w = case.w
+    if wfmt == "packed":
+        extra = lm.pack_weights(w["gate"], w["up"], w["down"])
+        wts = lm._weights(case.w_router, case.bias, None, None, None, None, extra)
+    elif wfmt == "fp8":
+        extra = lm.quantize_weights(w["gate"], w["up"], w["down"])
+        wts = lm._weights(case.w_router, case.bias, None, None, None, extra)
+    else:
+        wts = lm._weights(case.w_router, case.bias, w["gate"], w["up"], w["down"])
     dev = case.x.device
 
     def outs():
@@ -65,7 +76,11 @@ def test_forward_graph_replay(dtype, T, d, I):
         lm.lc_moe_forward(shape, x_other if name == "a" else case.x, wts, o["y"], o["idx"], o["gate"], o["load"], ws)
         torch.cuda.synchronize()
 
-    y_ref = oracle_forward(case)["y"]
+    if wfmt == "fp8":  # the oracle of the layer on the dequantized weights
+        from tests.test_gpu_fp8 import oracle_fp8_forward
+        y_ref = oracle_fp8_forward(case)["y"]
+    else:
+        y_ref = oracle_forward(case)["y"]
     err = rel_l2(to_np(eager["a"]["y"]), y_ref)
     say(f"  replays bitwise equal to eager; rel L2 vs oracle {err:.2e}")
     assert err <= (BF16_TOL if dtype == "bf16" else F32_TOL)
