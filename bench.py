@@ -402,7 +402,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": wl.description, "T": wl.T, "d": wl.d, "N": wl.N, "Z": wl.Z,
                    "K": wl.K, "I": wl.I, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "lcm::ffn_bf16_pipe_kernel<0, false> (gate/up + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "lcm::ffn_bf16_pipe_kernel<0, false, false> (gate/up + SwiGLU)",
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
                      "algorithmic_bytes": gu_bytes, "flops_per_launch": gu_flops,

@@ -159,7 +159,11 @@ def lc_moe_permute(shape, x, topk_idx, ffn_offsets, perm_token, slot_row, x_perm
 
 def _weights(w_router, bias, w_gate, w_up, w_down, fp8=None, packed=None) -> Weights:
     p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    return Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8), p(packed))
+    w = Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8), p(packed))
+    # the struct holds raw device addresses: keep the tensors alive as long as it lives, or
+    # a tensor made inline would go back to torch's allocator and be handed out again
+    w._tensors = (w_router, bias, w_gate, w_up, w_down, fp8, packed)
+    return w
 
 
 def lc_moe_fp8_weights_size(shape: Shape) -> int:

@@ -21,12 +21,20 @@ constexpr int kTokBlock = 256;  // tokens per permutation block
 // M-tile height (rows of one expert) of the grouped FFN kernels.
 constexpr int kBmBf16 = 128;  // ffn_bf16_kernel (any d, I multiple of 8)
 constexpr int kBmPipe = 320;  // ffn_bf16_pipe_kernel (d and I multiples of 32)
+constexpr int kBmSmall = 64;  // its few-row form, two workgroups per CU
+constexpr int kSmallMaxT = 256;  // layers of at most this many tokens run the few-row form
 constexpr int kBmF32 = 64;
 
 // The pipelined bf16 FFN kernel needs whole 32-element K steps in both GEMMs.
 inline bool ffn_pipelined(const lc_moe_shape& s) {
   return s.dtype == LC_MOE_BF16 && s.d % 32 == 0 && s.I % 32 == 0;
 }
+// Its few-row form runs for layers of few tokens (decode), whose experts get a few rows
+// each: there the 320-row form's single workgroup per CU leaves the loads idle while it
+// waits at its barriers, and two smaller workgroups per CU keep them busy.  An expert with
+// more than 64 rows (at most T) gets several M-tiles; they read the same weight tiles side
+// by side on one XCD, so the repeats come from its L2.
+inline bool ffn_small(const lc_moe_shape& s) { return ffn_pipelined(s) && s.T <= kSmallMaxT; }
 
 __device__ __forceinline__ float bf2f(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -102,7 +110,7 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   const size_t T = s.T, K = s.K, E = size_t(s.N) + s.Z, N = s.N;
   const size_t es = s.dtype == LC_MOE_BF16 ? 2 : 4;
   p.nblocks = int((T + kTokBlock - 1) / kTokBlock);
-  p.bm = s.dtype == LC_MOE_BF16 ? (ffn_pipelined(s) ? kBmPipe : kBmBf16) : kBmF32;
+  p.bm = s.dtype == LC_MOE_BF16 ? (ffn_pipelined(s) ? (ffn_small(s) ? kBmSmall : kBmPipe) : kBmBf16) : kBmF32;
   const size_t tk = T * K;
   size_t mt = N + (tk + p.bm - 1) / p.bm;
   if (mt > tk) mt = tk;

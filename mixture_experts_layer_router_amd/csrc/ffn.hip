@@ -218,7 +218,8 @@ __global__ __launch_bounds__(256, 2) void ffn_bf16_kernel(
 // Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4) through a
 // 160 KB ring whose stage holds the tile's activation rows (rounded up to 32) and the 256
 // weight rows, so few-row tiles get more stages; activation row groups past the tile's
-// rows are not loaded.
+// rows are not loaded.  Layers of few tokens run the few-row form (SMALL): 64-row tiles,
+// one row block per wave, half the ring, two workgroups per CU.
 // LDS row = 64 bytes = 4 chunks of 16 bytes; chunk c of row r sits in slot c ^ swz(r).
 // Software pipeline: a K step has two substeps of 16 (one MFMA deep).  While one substep
 // multiplies, the wave reads all its fragments of the next substep into the other
@@ -249,24 +250,27 @@ __device__ __forceinline__ bf16x8 dequant8(uint2 q, float scale) {
 // fp32 power-of-two scales (qscales; nrb_rows row blocks x nkb column blocks per matrix);
 // each weight fragment is converted to bf16 (v_cvt_scalef32_pk_bf16_fp8, exact) one
 // substep before its MFMAs, so the MFMAs see exactly the dequantized weights.
-template <int MODE, bool FP8>
-__global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
+// SMALL: the few-row form for layers whose experts get few rows (decode): M-tiles of 64
+// rows (one row block per wave) and an 80 KB ring, so two workgroups share a CU and one's
+// per-step chain of barrier, LDS reads, conversion and MFMAs runs while the other waits.
+template <int MODE, bool FP8, bool SMALL>
+__global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
     const bf16_t* __restrict__ a_src, const int32_t* __restrict__ perm_token,
     const bf16_t* __restrict__ w0, const bf16_t* __restrict__ w1,
     const unsigned char* __restrict__ qcodes, const float* __restrict__ qscales, int nrb_rows,
     int nkb, bf16_t* __restrict__ out, const MTile* __restrict__ mtiles,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_mtiles_ptr, int kdim,
     int ncols, int n_ntiles, int bpacked) {
-  constexpr int BM = kBmPipe;             // 320
+  constexpr int BM = SMALL ? kBmSmall : kBmPipe;  // 64 / 320
   constexpr int BK = 32;                  // K step
-  constexpr int LDS_BYTES = 160 * 1024;   // the ring
+  constexpr int LDS_BYTES = (SMALL ? 80 : 160) * 1024;  // the ring
   constexpr int MAX_NST = 16;             // ring stages at most
-  constexpr int MB = BM / 64;             // row blocks per wave (5)
+  constexpr int MB = BM / 64;             // row blocks per wave (5; few-row form 1)
   constexpr int RB = BK * 2;              // bytes per LDS activation row (64)
   constexpr int RPI = 16;                 // rows filled by one wave-wide load
-  constexpr int NIA = BM / RPI;           // activation loads per stage (20)
+  constexpr int NIA = BM / RPI;           // activation loads per stage (20; 4)
   constexpr int NIB = FP8 ? 8 : 256 / RPI;  // weight loads per stage (8 of 32 FP8 rows, 16)
-  constexpr int IA = (NIA + 7) / 8;       // activation load slots per wave (3)
+  constexpr int IA = (NIA + 7) / 8;       // activation load slots per wave (3; 1)
   constexpr int IB = NIB / 8;             // weight loads per wave (1, 2)
   constexpr int B_BYTES = FP8 ? 256 * 32 : 256 * RB;  // 8 KB / 16 KB
   __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
@@ -339,9 +343,10 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   const int bmul = bpacked ? 256 : 1;
   // Ring geometry from the tile's rows: a stage holds the activation rows the MFMAs read
   // (rows rounded up to 32) and the 256 weight rows, and the ring has as many stages as
-  // fit in 160 KB, up to 16 (bf16 weights: 4 at 320 rows, 5 at 256, 8 for decode-sized
-  // tiles; FP8 weights: 5 at 320 rows, 14 for decode-sized tiles).  Loads run that many
-  // stages ahead, so few-row tiles keep more weight bytes in flight.
+  // fit in its 160 KB (few-row form: 80 KB), up to 16 (bf16 weights: 4 at 320 rows, 5 at
+  // 256, 4 at up to 64 rows in 80 KB; FP8 weights: 5 at 320 rows, 8 at up to 32 rows in
+  // 80 KB).  Loads run that many stages ahead, so few-row tiles keep more weight bytes in
+  // flight.
   const int a_bytes = __builtin_amdgcn_readfirstlane(((rows + 31) & ~31) * RB);
   const int stage_bytes = a_bytes + B_BYTES;
   const int nst = LDS_BYTES / stage_bytes < MAX_NST ? LDS_BYTES / stage_bytes : MAX_NST;
@@ -515,13 +520,18 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
     for (int kt = nmain; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
     step(nk - 1, std::false_type{}, std::true_type{});
   };
-  switch (nvb) {
-    case 0: run(std::integral_constant<int, 0>{}); break;
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    case 2: run(std::integral_constant<int, 2>{}); break;
-    case 3: run(std::integral_constant<int, 3>{}); break;
-    case 4: run(std::integral_constant<int, 4>{}); break;
-    default: run(std::integral_constant<int, 5>{}); break;
+  if constexpr (MB == 1) {
+    if (nvb == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    switch (nvb) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      default: run(std::integral_constant<int, 5>{}); break;
+    }
   }
 
   // epilogue; 32x32 D layout: column lane & 31, rows 8*(r/4) + 4*(lane/32) + r%4
@@ -552,16 +562,20 @@ __global__ __launch_bounds__(512, 1) void ffn_bf16_pipe_kernel(
   }
 }
 
-#define LCM_INST(M, Q)                                                                        \
-  template __global__ void ffn_bf16_pipe_kernel<M, Q>(                                        \
+#define LCM_INST(M, Q, S)                                                                     \
+  template __global__ void ffn_bf16_pipe_kernel<M, Q, S>(                                     \
       const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,    \
       const bf16_t* __restrict__, const unsigned char* __restrict__, const float* __restrict__, \
       int, int, bf16_t* __restrict__, const MTile* __restrict__, const int32_t* __restrict__, \
       const int32_t* __restrict__, int, int, int, int);
-LCM_INST(0, false)
-LCM_INST(1, false)
-LCM_INST(0, true)
-LCM_INST(1, true)
+LCM_INST(0, false, false)
+LCM_INST(1, false, false)
+LCM_INST(0, true, false)
+LCM_INST(1, true, false)
+LCM_INST(0, false, true)
+LCM_INST(1, false, true)
+LCM_INST(0, true, true)
+LCM_INST(1, true, true)
 #undef LCM_INST
 
 // ---------------------------------------------------------------------------------------
@@ -625,6 +639,16 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
     }
 }
 
+// The instantiation of the pipelined kernel for the layer: its few-row form for layers of
+// few tokens, else the 320-row form (the M-tile list was built with the matching height).
+using PipeKernel = void (*)(const bf16_t*, const int32_t*, const bf16_t*, const bf16_t*,
+                            const unsigned char*, const float*, int, int, bf16_t*, const MTile*,
+                            const int32_t*, const int32_t*, int, int, int, int);
+template <int MODE, bool FP8>
+PipeKernel pipe_kernel(const lc_moe_shape& s) {
+  return ffn_small(s) ? ffn_bf16_pipe_kernel<MODE, FP8, true> : ffn_bf16_pipe_kernel<MODE, FP8, false>;
+}
+
 hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
                               const void* w_gate, const void* w_up, const void* fp8,
                               const void* packed, void* hbuf, const MTile* mtiles,
@@ -637,18 +661,18 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
     const Fp8Plan q = plan_fp8(s);
     const unsigned char* qb = static_cast<const unsigned char*>(fp8);
     if (fp8)
-      ffn_bf16_pipe_kernel<0, true><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<0, true>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, nullptr, nullptr, qb + q.codes_gu,
           reinterpret_cast<const float*>(qb + q.scales_gu), q.nrb_i, q.nrb_d,
           static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
     else if (packed)
-      ffn_bf16_pipe_kernel<0, false><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<0, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token,
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).gu),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
           s.I, nn, 1);
     else
-      ffn_bf16_pipe_kernel<0, false><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<0, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
           static_cast<const bf16_t*>(w_up), nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf),
           mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
@@ -683,18 +707,18 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
     const Fp8Plan q = plan_fp8(s);
     const unsigned char* qb = static_cast<const unsigned char*>(fp8);
     if (fp8)
-      ffn_bf16_pipe_kernel<1, true><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<1, true>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, nullptr, nullptr, qb + q.codes_d,
           reinterpret_cast<const float*>(qb + q.scales_d), q.nrb_d, q.nrb_i,
           static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn, 0);
     else if (packed)
-      ffn_bf16_pipe_kernel<1, false><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<1, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr,
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).d),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I,
           s.d, nn, 1);
     else
-      ffn_bf16_pipe_kernel<1, false><<<dim3(grid), dim3(512), 0, st>>>(
+      pipe_kernel<1, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
           nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d,
           nn, 0);
