@@ -309,7 +309,8 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
     srcQ = reinterpret_cast<const bf16_t*>(qcodes + (size_t(e) * n_ntiles + ntile) * (kdim / BK) * size_t(8192) +
                                            wave * 1024 + lane * 16);
   } else if (bpacked) {
-    // packed bf16: weight load q is the 1 KB piece q of the stage's 16 KB block
+    // packed bf16: weight load q is the 1 KB piece q of the stage's 16 KB block (the block
+    // of K step k starts k * 8192 elements, i.e. kphys * 256, into the unit's blocks)
 #pragma unroll
     for (int i = 0; i < IB; ++i)
       srcB[i] = w0 + (size_t(e) * n_ntiles + ntile) * (kdim / BK) * size_t(8192) + (wave + 8 * i) * 512 +
@@ -338,9 +339,6 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
   // spread over the memory channels.
   const int krot = (j * 7 + ntile * 3) % nk;
   auto kphys = [&](int kt) { const int k = kt + krot; return (k >= nk ? k - nk : k) * BK; };
-  // source elements per K element of the weight loads: 1 row-major, 256 packed (one 8192-
-  // element block per 32-wide K step)
-  const int bmul = bpacked ? 256 : 1;
   // Ring geometry from the tile's rows: a stage holds the activation rows the MFMAs read
   // (rows rounded up to 32) and the 256 weight rows, and the ring has as many stages as
   // fit in its 160 KB (few-row form: 80 KB), up to 16 (bf16 weights: 4 at 320 rows, 5 at
@@ -355,10 +353,12 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
     unsigned char* st = smem + slot * stage_bytes;
     if (i < IA) {
       if (i < na) dma16(srcA[i] + kphys(kt), st + (wave + 8 * i) * 1024);
-    } else if (FP8) {
-      dma16(srcQ + size_t(kphys(kt)) * 128, st + a_bytes + wave * 1024);  // 8 KB per stage
+    } else if (FP8) {  // the packed layouts are read once in whole lines: streaming loads
+      dma16_stream(srcQ + size_t(kphys(kt)) * 128, st + a_bytes + wave * 1024);  // 8 KB per stage
+    } else if (bpacked) {
+      dma16_stream(srcB[i - IA] + size_t(kphys(kt)) * 256, st + a_bytes + (wave + 8 * (i - IA)) * 1024);
     } else {
-      dma16(srcB[i - IA] + kphys(kt) * bmul, st + a_bytes + (wave + 8 * (i - IA)) * 1024);
+      dma16(srcB[i - IA] + kphys(kt), st + a_bytes + (wave + 8 * (i - IA)) * 1024);
     }
   };
   // wait until this wave's loads of stage s landed, `newest` being the last stage issued

@@ -13,6 +13,15 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
+// The same with the non-temporal hint (cache-policy bit NT): for data read exactly once
+// in whole 128-byte lines, such as weights stored in the order a kernel streams them.
+// The hint keeps the stream from displacing reused lines; a stream that reads half a line
+// per load and the other half a step later (row-major weights, 64-byte segments) must
+// not take it, or each line is fetched twice.
+__device__ __forceinline__ void dma16_stream(const void* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 2);
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define LCM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14)))
 
