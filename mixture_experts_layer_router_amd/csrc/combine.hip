@@ -1,19 +1,25 @@
-// Fused combine: y_t = sum over the token's picks, in pick order, of g * E_i(x_t), where
-// E_i(x_t) is the FFN expert's output row for an FFN pick and x_t itself for a
-// zero-computation pick (LongCat-Flash article, itouyu.top, section "Zero-computation
-// experts": the identity expert returns its input).  fp32 accumulation, one rounding to
-// the output dtype.  One workgroup per token; 16-byte vector loads along d.
+// Fused combine: y_t = sum over the token's FFN picks, in pick order, of g * E_i(x_t),
+// plus (sum of the gates of its zero-computation picks, in pick order) * x_t
+// (LongCat-Flash article, itouyu.top, section "Zero-computation experts": the identity
+// expert returns its input, so all of a token's zero picks together add their gates times
+// x_t).  fp32 accumulation, one rounding to the output dtype.  One workgroup per token;
+// 16-byte vector loads along d; x_t is read once, after the FFN rows.
 #include "common.h"
 
 namespace lcm {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 bf16 -> fp32.  STREAM: non-temporal load, for the FFN output rows, which are read
+// exactly once here (whole rows, whole lines); x rows may be read again by later picks.
+template <bool STREAM>
 __device__ __forceinline__ void load8(const bf16_t* p, float* v) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const u32x4* q4 = reinterpret_cast<const u32x4*>(p);
+  const u32x4 q = STREAM ? __builtin_nontemporal_load(q4) : *q4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
   }
 }
 
@@ -26,14 +32,24 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restr
   const bf16_t* xt = x + size_t(t) * d;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float gz = 0.f;  // sum of the zero picks' gates
     for (int k = 0; k < K; ++k) {
       const float g = gate[size_t(t) * K + k];
       const int r = slot_row[size_t(t) * K + k];
-      const bf16_t* src = r >= 0 ? ybuf + size_t(r) * d : xt;
-      float v[8];
-      load8(src + c, v);
+      if (r >= 0) {
+        float v[8];
+        load8<true>(ybuf + size_t(r) * d + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      } else {
+        gz += g;
+      }
+    }
+    if (gz != 0.f) {
+      float v[8];
+      load8<false>(xt + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gz, v[i], acc[i]);
     }
     uint32_t o[4];
 #pragma unroll
@@ -51,14 +67,26 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   const float* xt = x + size_t(t) * d;
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float gz = 0.f;  // sum of the zero picks' gates
     for (int k = 0; k < K; ++k) {
       const float g = gate[size_t(t) * K + k];
       const int r = slot_row[size_t(t) * K + k];
-      const float4 v = *reinterpret_cast<const float4*>((r >= 0 ? ybuf + size_t(r) * d : xt) + c);
+      if (r < 0) {
+        gz += g;
+        continue;
+      }
+      const float4 v = *reinterpret_cast<const float4*>(ybuf + size_t(r) * d + c);
       acc.x = fmaf(g, v.x, acc.x);
       acc.y = fmaf(g, v.y, acc.y);
       acc.z = fmaf(g, v.z, acc.z);
       acc.w = fmaf(g, v.w, acc.w);
+    }
+    if (gz != 0.f) {
+      const float4 v = *reinterpret_cast<const float4*>(xt + c);
+      acc.x = fmaf(gz, v.x, acc.x);
+      acc.y = fmaf(gz, v.y, acc.y);
+      acc.z = fmaf(gz, v.z, acc.z);
+      acc.w = fmaf(gz, v.w, acc.w);
     }
     *reinterpret_cast<float4*>(y + size_t(t) * d + c) = acc;
   }
