@@ -403,12 +403,26 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + size_t(t) * E;
-  float v[EPL];
+  // All loads first, unconditionally (slots past E read expert E-1 and are masked below),
+  // so they are in flight together: loads under per-slot branches each waited on their own,
+  // and a token's chain then took one memory latency per slot.
+  float v[EPL], b[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    const int ec = e < E ? e : E - 1;
+    v[j] = row[ec];
+    b[j] = bias[ec];
+  }
+  // keeps the bias loads here: left alone, the compiler sinks them to their use after the
+  // softmax, a second memory round trip on each token's chain
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) asm volatile("" : "+v"(v[j]), "+v"(b[j]));
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : -INFINITY;
+    v[j] = e < E ? v[j] : -INFINITY;
     m = fmaxf(m, v[j]);
   }
   // wavefront reductions (DPP, fixed order; every lane gets the same result)
@@ -426,7 +440,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     v[j] = v[j] / sum;  // p, IEEE division
-    s[j] = e < E ? v[j] + bias[e] : -INFINITY;
+    s[j] = e < E ? v[j] + b[j] : -INFINITY;
   }
   // K rounds: the largest s left wins, the lowest expert index among equal s.  Each round
   // takes the lane's best remaining slot (ascending slots keep the lower index), the
