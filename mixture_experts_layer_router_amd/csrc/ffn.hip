@@ -579,6 +579,193 @@ LCM_INST(1, true, true)
 #undef LCM_INST
 
 // ---------------------------------------------------------------------------------------
+// Whole-line kernel: the few-row form for row-major bf16 weights (layers of at most 256
+// tokens, K a multiple of 64).  The 320-row and few-row forms above stage 32 K elements of
+// 256 weight rows, i.e. half of each row's 128-byte line per stage, and the other half one
+// stage later: the line has to stay in the L2 in between, and a decode layer streamed its
+// weights at 72-75% of the HBM peak.  Here a stage holds 64 K elements of 128 weight rows
+// -- whole lines, read once, so they take the streaming hint -- and the two halves of the
+// tile's 256 weight rows alternate:
+//   MODE 0: even stages gate rows n0..n0+127, odd stages up rows n0..n0+127;
+//   MODE 1: even stages W_down rows n0..n0+127, odd stages n0+128..n0+255.
+// A stage also holds the tile's activation rows for its 64 K elements (read from L2 by both
+// stages of the pair).  LDS rows are 128 bytes = 8 chunks; chunk c of row r sits in slot
+// c ^ swz8(r), which spreads the 16 rows a read phase touches over all 64 banks.
+// 512 threads = 8 waves, two workgroups per CU: wave w owns the 32-row block w >> 2 of the
+// 64-row tile against the 32 weight rows 32 * (w & 3) of each half; a stage is 4 substeps
+// of 16.  Ring, waits and barriers as in the kernel above.
+// ---------------------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+template <int MODE>
+__global__ __launch_bounds__(512, 2) void ffn_bf16_line_kernel(
+    const bf16_t* __restrict__ a_src, const int32_t* __restrict__ perm_token,
+    const bf16_t* __restrict__ w0, const bf16_t* __restrict__ w1, bf16_t* __restrict__ out,
+    const MTile* __restrict__ mtiles, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ n_mtiles_ptr, int kdim, int ncols, int n_ntiles) {
+  constexpr int BM = kBmSmall;          // 64 rows
+  constexpr int BK = 64;                // K elements per stage
+  constexpr int RB = BK * 2;            // bytes per LDS row (128)
+  constexpr int LDS_BYTES = 80 * 1024;  // the ring
+  constexpr int MAX_NST = 16;
+  constexpr int B_BYTES = 128 * RB;     // 16 KB: one half's 128 weight rows
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+  int j, ntile;
+  if (!unit_of_block(mtiles, offsets, *n_mtiles_ptr, n_ntiles, BM, j, ntile)) return;
+  const MTile tile = mtiles[j];
+  const int e = tile.expert, row0 = tile.row0, rows = tile.rows;
+  const int n0 = ntile * (MODE == 0 ? 128 : 256);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lrow = lane >> 3, lslot = lane & 7;
+
+  // Activation load of wave w: LDS rows 8w..8w+7 (lane l: row 8w + l/8, slot l%8, global
+  // chunk (l%8) ^ swz8(row)); skipped when all 8 rows lie past the tile's rows.
+  const int na = wave * 8 < rows ? 1 : 0;
+  const int ra = wave * 8 + lrow;
+  const int ar = ra < rows ? ra : 0;  // rows past the tile read a valid row; never stored
+  const size_t a_row = MODE == 0 ? size_t(perm_token[row0 + ar]) : size_t(row0 + ar);
+  const bf16_t* srcA = a_src + a_row * kdim + (lslot ^ swz8(ra)) * 8;
+  // Weight load i of wave w in half h: rows 8(w + 8i)..+7 of the half's 128 rows.
+  const bf16_t* srcB[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (wave + 8 * i) * 8 + lrow;  // 0..127
+      const int c = MODE == 0 ? n0 + r : n0 + h * 128 + r;
+      const bf16_t* mat = MODE == 0 ? (h ? w1 : w0) : w0;
+      const int brow = c < ncols ? c : n0;  // rows past the matrix repeat a valid row
+      srcB[h][i] = mat + (size_t(e) * ncols + brow) * kdim + (lslot ^ swz8(r)) * 8;
+    }
+  const int per_stage = na + 2;  // this wave's loads per stage
+  const int nk = kdim / BK;      // K chunks
+  const int total = 2 * nk;      // stages: two halves per K chunk
+  // each work unit starts its K loop at its own chunk (spreads tiles over the channels)
+  const int krot = (j * 7 + ntile * 3) % nk;
+  auto kphys = [&](int kt) { const int k = (kt >> 1) + krot; return (k >= nk ? k - nk : k) * BK; };
+  const int a_bytes = __builtin_amdgcn_readfirstlane(((rows + 31) & ~31) * RB);
+  const int stage_bytes = a_bytes + B_BYTES;
+  const int nst = LDS_BYTES / stage_bytes < MAX_NST ? LDS_BYTES / stage_bytes : MAX_NST;  // 4 (<= 32 rows), 3
+  auto issue_one = [&](int i, int kt, int slot) {
+    unsigned char* st = smem + slot * stage_bytes;
+    if (i == 0) {
+      if (na) dma16(srcA + kphys(kt), st + wave * 1024);
+    } else {
+      const bf16_t* g = (kt & 1) ? srcB[1][i - 1] : srcB[0][i - 1];
+      dma16_stream(g + kphys(kt), st + a_bytes + (wave + 8 * (i - 1)) * 1024);
+    }
+  };
+  auto wait_stage = [&](int s, int newest) { wait_vmcnt((newest - s) * per_stage); };
+
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int arow = wm * 32 + l32, brow_l = wn * 32 + l32;
+  const int sa = swz8(arow), sb = swz8(brow_l);
+  const bool active = wm * 32 < rows;  // this wave's row block holds tile rows
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[h][r] = 0.f;
+
+  const int npro = total < nst ? total : nst;
+  for (int s2 = 0; s2 < npro; ++s2)
+    for (int i = 0; i < 3; ++i) issue_one(i, s2, s2);
+
+  auto run = [&](auto act_tag) {
+    constexpr bool ACT = decltype(act_tag)::value;
+    auto rd = [&](int ring_slot, int ks, bf16x8& a, bf16x8& b) {
+      if constexpr (ACT) {
+        const unsigned char* st = smem + ring_slot * stage_bytes;
+        const int c = ks * 2 + khalf;
+        a = *reinterpret_cast<const bf16x8*>(st + arow * RB + ((c ^ sa) << 4));
+        b = *reinterpret_cast<const bf16x8*>(st + a_bytes + brow_l * RB + ((c ^ sb) << 4));
+      }
+    };
+    // MFMA of one substep into the half's accumulator; with DMA, this wave's loads of
+    // stage kt_load go out behind it
+    auto mm = [&](auto h_tag, const bf16x8& a, const bf16x8& b, bool dma, int kt_load, int slot) {
+      constexpr int H = decltype(h_tag)::value;
+      if constexpr (ACT) acc[H] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[H], 0, 0, 0);
+      if (dma)
+        for (int i = 0; i < 3; ++i) issue_one(i, kt_load, slot);
+    };
+    bf16x8 ca, cb, xa, xb;
+    wait_stage(0, npro - 1);
+    block_barrier();
+    rd(0, 0, ca, cb);
+    int sk = 0;
+    auto step = [&](int kt, auto h_tag, auto last_tag) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      const int sk1 = sk + 1 == nst ? 0 : sk + 1;
+      rd(sk, 1, xa, xb);
+      mm(h_tag, ca, cb, false, 0, 0);
+      rd(sk, 2, ca, cb);
+      mm(h_tag, xa, xb, false, 0, 0);
+      rd(sk, 3, xa, xb);
+      mm(h_tag, ca, cb, false, 0, 0);
+      if (!LAST) {
+        wait_lds_reads();  // this wave's reads of stage kt done
+        const int newest = kt + nst - 1 < total - 1 ? kt + nst - 1 : total - 1;
+        wait_stage(kt + 1, newest);
+        block_barrier();  // stage kt+1 visible to all waves; nobody reads stage kt again
+        rd(sk1, 0, ca, cb);
+      }
+      mm(h_tag, xa, xb, kt + nst < total, kt + nst, sk);  // stage kt+nst takes stage kt's slot
+      sk = sk1;
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    for (int kt = 0; kt < total - 2; kt += 2) {
+      step(kt, H0{}, std::false_type{});
+      step(kt + 1, H1{}, std::false_type{});
+    }
+    step(total - 2, H0{}, std::false_type{});
+    step(total - 1, H1{}, std::true_type{});
+  };
+  if (active) run(std::true_type{});
+  else run(std::false_type{});
+
+  if (!active) return;
+  // epilogue; 32x32 D layout: column lane & 31, rows 8*(r/4) + 4*(lane/32) + r%4
+  if (MODE == 0) {
+    const int col = n0 + wn * 32 + l32;
+    if (col < ncols) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < rows) out[size_t(row0 + row) * ncols + col] = f2bf(swiglu_fast(acc[0][r], acc[1][r]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0 + h * 128 + wn * 32 + l32;
+      if (col >= ncols) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < rows) out[size_t(row0 + row) * ncols + col] = f2bf(acc[h][r]);
+      }
+    }
+  }
+}
+
+template __global__ void ffn_bf16_line_kernel<0>(const bf16_t* __restrict__, const int32_t* __restrict__,
+                                                 const bf16_t* __restrict__, const bf16_t* __restrict__,
+                                                 bf16_t* __restrict__, const MTile* __restrict__,
+                                                 const int32_t* __restrict__, const int32_t* __restrict__, int,
+                                                 int, int);
+template __global__ void ffn_bf16_line_kernel<1>(const bf16_t* __restrict__, const int32_t* __restrict__,
+                                                 const bf16_t* __restrict__, const bf16_t* __restrict__,
+                                                 bf16_t* __restrict__, const MTile* __restrict__,
+                                                 const int32_t* __restrict__, const int32_t* __restrict__, int,
+                                                 int, int);
+
+// ---------------------------------------------------------------------------------------
 // fp32 kernel (FMA): tile 64 rows x 64 output columns, K step 16, 4x4 outputs per thread.
 // MODE 0 keeps gate and up accumulators for the same columns.
 // ---------------------------------------------------------------------------------------
@@ -671,6 +858,11 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).gu),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
           s.I, nn, 1);
+    else if (ffn_small(s) && s.d % 64 == 0)
+      ffn_bf16_line_kernel<0><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
+          static_cast<const bf16_t*>(w_up), static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
+          s.I, nn);
     else
       pipe_kernel<0, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
@@ -717,6 +909,10 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).d),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I,
           s.d, nn, 1);
+    else if (ffn_small(s) && s.I % 64 == 0)
+      ffn_bf16_line_kernel<1><<<dim3(grid), dim3(512), 0, st>>>(
+          static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
+          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn);
     else
       pipe_kernel<1, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,

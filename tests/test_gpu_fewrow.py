@@ -1,9 +1,11 @@
-"""The few-row form of the pipelined FFN kernel (64-row M-tiles, two workgroups per CU),
-which runs for layers of at most 256 tokens, against the oracle on every weight format,
-with routing skewed so that experts get more rows than one 64-row M-tile holds (several
-M-tiles reading one weight tile), ragged n-tiles (I % 128, d % 256) and single rows.
-T = 257 and 65 sit on either side of the switch to the 320-row form and of one 64-row
-M-tile; both forms must give the oracle's results."""
+"""The few-row FFN kernels (64-row M-tiles, two workgroups per CU), which run for layers of
+at most 256 tokens, against the oracle on every weight format, with routing skewed so that
+experts get more rows than one 64-row M-tile holds (several M-tiles reading one weight
+tile), ragged n-tiles (I % 128, d % 256) and single rows.  T = 257 and 65 sit on either
+side of the switch to the 320-row form and of one 64-row M-tile; both forms must give the
+oracle's results.  Row-major weights with K a multiple of 64 (d for gate/up, I for down)
+take the whole-line kernel: d=320, I=192 (ragged n-tiles in both GEMMs) and d=I=64 (one K
+chunk: two stages) reach it; d=288, I=160 keep the pipelined kernel's few-row form."""
 import numpy as np
 import pytest
 
@@ -16,11 +18,12 @@ HOT = (3, 9)  # FFN experts every token selects (bias far above the rest)
 
 @pytest.mark.parametrize("T", [256, 257, 64, 65, 1])
 @pytest.mark.parametrize("wfmt", ["rows", "packed", "fp8"])
-def test_fewrow_skewed_against_oracle(T, wfmt):
+@pytest.mark.parametrize("d,I", [(288, 160), (320, 192), (64, 64)])
+def test_fewrow_skewed_against_oracle(T, wfmt, d, I):
     import torch
     import mixture_experts_layer_router_amd as lm
-    d, I, N, Z, K = 288, 160, 20, 6, 4
-    wl = adhoc(name=f"fewrow_{T}_{wfmt}", T=T, d=d, N=N, Z=Z, K=K, I=I, seed_key=(430, T),
+    N, Z, K = 20, 6, 4
+    wl = adhoc(name=f"fewrow_{T}_{wfmt}_{d}_{I}", T=T, d=d, N=N, Z=Z, K=K, I=I, seed_key=(430, T, d),
                expert_std=1 / np.sqrt(d))
 
     def modify(ri):

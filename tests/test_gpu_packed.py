@@ -1,13 +1,15 @@
 """Packed bf16 expert weights on the GPU: lc_moe_pack_weights writes the documented tile
 layout (checked against an independent re-layout of the weights in numpy, bit for bit,
 including the zero padding of ragged n-tiles), and the layer run on the packed weights
-equals the layer run on the row-major weights bit for bit -- the packed form only changes
-where the kernel reads each weight from."""
+equals the layer run on the row-major weights bit for bit wherever both run the pipelined
+kernel -- the packed form only changes where that kernel reads each weight from.  Where the
+row-major weights take the whole-line few-row kernel instead, which adds the K steps in
+another order, both layers are checked against the oracle and against each other."""
 import numpy as np
 import pytest
 
 from inputs import configs
-from tests.gpu_common import adhoc, audited, make_case, say, to_np
+from tests.gpu_common import BF16_TOL, adhoc, audited, make_case, oracle_forward, rel_l2, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +76,12 @@ def run_both(case, K):
     return a, b
 
 
+def line_kernel_runs(T, d, I):
+    """Whether the row-major weights take the whole-line few-row kernel in either GEMM
+    (layers of at most 256 tokens; gate/up needs d % 64 == 0, down I % 64 == 0)."""
+    return T <= 256 and (d % 64 == 0 or I % 64 == 0)
+
+
 def assert_same(a, b):
     import torch
     for k in ("topk_idx", "topk_gate", "load"):
@@ -81,9 +89,27 @@ def assert_same(a, b):
     assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
 
 
+def assert_pair(case, a, b, tokens=None):
+    """Bit for bit where both formats run the same kernel; otherwise identical routing and
+    both outputs within the bf16 tolerance of the oracle (on `tokens`, all by default)."""
+    import torch
+    wl = case.wl
+    if not line_kernel_runs(case.x.shape[0], wl.d, wl.I):
+        assert_same(a, b)
+        return
+    for k in ("topk_idx", "topk_gate", "load"):
+        assert torch.equal(a[k], b[k]), k
+    ref = oracle_forward(case, tokens=tokens)
+    sel = slice(None) if tokens is None else tokens
+    ya, yb = to_np(a["y"])[sel], to_np(b["y"])[sel]
+    ea, eb, eab = rel_l2(ya, ref["y"]), rel_l2(yb, ref["y"]), rel_l2(ya, yb)
+    say(f"  row-major vs oracle {ea:.2e}, packed vs oracle {eb:.2e}, row-major vs packed {eab:.2e}")
+    assert ea <= BF16_TOL and eb <= BF16_TOL
+
+
 @pytest.mark.parametrize("T,d,I,N,Z,K", [(300, 256, 160, 12, 5, 4), (96, 288, 384, 40, 20, 6),
                                          (1, 64, 32, 3, 1, 2), (1200, 128, 96, 6, 2, 3)])
-def test_forward_packed_bitwise_equal(T, d, I, N, Z, K):
+def test_forward_packed_matches_row_major(T, d, I, N, Z, K):
     """Ragged gate/up n-tiles (I % 128), ragged down n-tiles (d % 256), one token, and
     experts with more than 320 rows (two M-tiles)."""
     wl = adhoc(name=f"pk{T}", T=T, d=d, N=N, Z=Z, K=K, I=I, seed_key=(411, T), expert_std=1 / np.sqrt(d))
@@ -92,13 +118,13 @@ def test_forward_packed_bitwise_equal(T, d, I, N, Z, K):
     a, b = run_both(case, K)
     if T == 1200:
         assert int(to_np(a["load"])[:N].max()) > 320
-    assert_same(a, b)
+    assert_pair(case, a, b)
 
 
 @pytest.mark.parametrize("name", ["decode_T64_z33", "prefill"])
-def test_forward_packed_full_size_bitwise_equal(name):
+def test_forward_packed_full_size_matches_row_major(name):
     wl = configs.get(name)
     say(f"packed forward full size: {wl.description}")
     case = make_case(wl)
     a, b = run_both(case, wl.K)
-    assert_same(a, b)
+    assert_pair(case, a, b, tokens=list(range(0, wl.T, max(1, wl.T // 6))))
