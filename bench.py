@@ -22,8 +22,8 @@ decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); t
 one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
 graph and replayed (graph_ms_per_step), run on packed bf16 expert weights (packed_*), and
 run on block-FP8 expert weights (fp8_*).
-prefill_packed: the prefill layer on packed bf16 expert weights (lc_moe_pack_weights; the
-same bits as the row-major weights).
+prefill_packed: the prefill layer on packed bf16 expert weights (lc_moe_pack_weights; at
+this size the same bits as the row-major weights).
 prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
 overlap: a dense SwiGLU FFN (width 2d) over the same tokens beside the layer, serial on one
 stream against concurrent on two streams.
@@ -109,7 +109,7 @@ def use_fp8(lm, st):
 
 def use_packed(lm, st):
     """Re-lay the layer's bf16 expert weights in the packed tile layout and point the
-    forward at them (the same values; the layer computes the same bits)."""
+    forward at them (the same values)."""
     import torch
     st["packed"] = lm.pack_weights(st["w"]["gate"], st["w"]["up"], st["w"]["down"])
     st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"], None,

@@ -2,7 +2,8 @@
 // becomes one contiguous 16 KB block holding exactly the LDS image of that stage's 256
 // weight rows (layout in common.h, plan_packed).  The kernel then fills a stage with 16
 // one-kilobyte contiguous loads instead of 256 row segments 64 bytes long.  The values are
-// copied bit for bit, so the layer computed on the packed weights is the same, to the bit.
+// copied bit for bit; where the row-major weights run the same pipelined kernel (layers of
+// more than 256 tokens) the layer computed on the packed weights is the same, to the bit.
 #include "common.h"
 
 namespace lcm {
