@@ -6,7 +6,8 @@
 One step = one lc_moe_forward (router, permutation, grouped SwiGLU FFN, combine) over the
 workload's resident inputs.  Prints ONE JSON line.  value = tokens/s of the whole layer
 (inputs and weights already in HBM).  Per-stage times come from HIP events recorded by
-lc_moe_forward_staged on the launch stream inside the timed region.
+lc_moe_forward_staged on the launch stream inside the timed region; step_ms_percentiles
+gives p10/p50/p90 of the timed steps' spans (first to last stage event of each step).
 
 roofline: the dominant kernel is the gate/up grouped GEMM (ffn_bf16_pipe_kernel<0>: two
 thirds of the FFN FLOPs and weight bytes).  At this shape its HBM floor (algorithmic bytes
@@ -123,7 +124,8 @@ def drop_packed(lm, st):
 
 
 def run_steps(lm, st, steps, warmup):
-    """Warm up, then time exactly `steps` forwards; returns (total_ms, per-stage ms lists)."""
+    """Warm up, then time exactly `steps` forwards; returns (total_ms, per-stage ms lists).
+    Each step's span (first to last stage event) is left in st["step_ms"]."""
     import torch
     o = st["outs"]
 
@@ -148,6 +150,7 @@ def run_steps(lm, st, steps, warmup):
     total = start.elapsed_time(stop)
     stages = {lm.stage_name(s): [evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)]
               for s in range(nst)}
+    st["step_ms"] = [evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)]
     return total, stages
 
 
@@ -371,6 +374,7 @@ def main():
     log("inputs resident")
     total, stages = run_steps(lm, st, args.steps, args.warmup)
     ms = total / args.steps
+    step_pct = {f"p{q}": float(np.percentile(st["step_ms"], q)) for q in (10, 50, 90)}
     load = st["outs"]["load"].cpu().numpy()
     nnz = int(load[:wl.N].sum())
     touched = int((load[:wl.N] > 0).sum())
@@ -414,6 +418,7 @@ def main():
                 "mfma_frac": ffn_tflops / MFMA_BF16_PEAK_TFLOPS,
                 "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
         "stages_ms": st_ms,
+        "step_ms_percentiles": step_pct,
     }
     if not args.no_packed:
         use_packed(lm, st)
