@@ -138,11 +138,12 @@ def test_forward_fp8_matches_oracle(T, d, I, N, Z, K):
     assert err <= BF16_TOL
 
 
-def test_forward_fp8_decode_full_size_sampled():
+@pytest.mark.parametrize("name", ["decode_T64_z66", "decode_T256_z66"])
+def test_forward_fp8_decode_full_size_sampled(name):
     """The decode layer at full size (768-expert pool, d=6144, I=2048) on FP8 weights; the
     oracle checks two sampled tokens (their experts quantized by the oracle)."""
     import mixture_experts_layer_router_amd as lm
-    wl = configs.get("decode_T64_z66")
+    wl = configs.get(name)
     say(f"fp8 forward full size: {wl.description}")
     case = make_case(wl)
     q = quantize_on_gpu(case.w)

@@ -16,7 +16,8 @@ from inputs import configs
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny", "small", "decode_T64_z0", "decode_T128_z33", "decode_T256_z66"]
+# every decode layer (T <= 256: the few-row kernels) at full size, on sampled tokens
+SMALL = ["tiny", "small"] + [f"decode_T{T}_z{z}" for T in configs.DECODE_T for z in configs.DECODE_SHARES]
 ALL_NAMED = list(configs.WORKLOADS)
 
 
