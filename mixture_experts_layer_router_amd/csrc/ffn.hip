@@ -13,6 +13,16 @@
 // expert by expert, n-tile-major inside an expert (the M-tiles that share one weight tile
 // are adjacent), and each XCD takes one contiguous eighth of that order, so the tiles
 // that share weights or activations run together on one XCD and meet in its L2.
+//
+// Kernels, by layer:
+//   ffn_bf16_pipe_kernel<MODE, FP8, false>  bf16, d and I multiples of 32, more than 256
+//                                           tokens: 320-row tiles, one workgroup per CU
+//   ffn_bf16_pipe_kernel<MODE, FP8, true>   the same for at most 256 tokens on packed or
+//                                           block-FP8 weights: 64-row tiles, two per CU
+//   ffn_bf16_line_kernel<MODE>              at most 256 tokens on row-major weights with K
+//                                           a multiple of 64: whole-line stages
+//   ffn_bf16_kernel<MODE>                   other bf16 shapes (multiples of 8)
+//   ffn_f32_kernel<MODE>                    fp32 layers
 #include <type_traits>
 
 #include "common.h"
