@@ -33,7 +33,32 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const bf16_t* __restr
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float gz = 0.f;  // sum of the zero picks' gates
-    for (int k = 0; k < K; ++k) {
+    // Picks in groups of 4: the 4 row loads go out together, unconditionally (a zero pick
+    // reads FFN output row 0 and ignores it), then the terms are added in pick order.  With
+    // the loads under per-pick branches each waited on its own, and a layer of few tokens,
+    // which has nothing else to overlap, took one memory latency per pick.
+    int k = 0;
+    for (; k + 4 <= K; k += 4) {
+      float g[4], v[4][8];
+      int r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g[i] = gate[size_t(t) * K + k + i];
+        r[i] = slot_row[size_t(t) * K + k + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load8<true>(ybuf + size_t(r[i] >= 0 ? r[i] : 0) * d + c, v[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (r[i] >= 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(g[i], v[i][e], acc[e]);
+        } else {
+          gz += g[i];
+        }
+      }
+    }
+    for (; k < K; ++k) {
       const float g = gate[size_t(t) * K + k];
       const int r = slot_row[size_t(t) * K + k];
       if (r >= 0) {
