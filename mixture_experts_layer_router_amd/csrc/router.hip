@@ -445,29 +445,29 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   // K rounds: the largest s left wins, the lowest expert index among equal s.  Each round
   // takes the lane's best remaining slot (ascending slots keep the lower index), the
   // wavefront maximum of those, then the lowest expert index holding that maximum.
+  // Branch-free: slots past E and taken slots hold -inf, so "the first remaining slot, then
+  // any strictly larger one" is s > bv from bv = -inf (equal s keep the lower slot).
   for (int k = 0; k < K; ++k) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && s[j] != -INFINITY && (s[j] > bv || be == 0x7fffffff)) {
-        bv = s[j];
-        be = e;
-      }
+      const bool better = s[j] > bv;
+      bv = better ? s[j] : bv;
+      be = better ? lane + 64 * j : be;
     }
     const float wm = __ockl_wfred_max_f32(bv);
     const int we = __ockl_wfred_min_i32(bv == wm ? be : 0x7fffffff);
-    if ((we & 63) == lane) {
-      const int j = we >> 6;
-      float p = 0.f;
+    const bool mine = (we & 63) == lane;
+    const int jw = we >> 6;
+    float p = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < EPL; ++jj) {
-        if (jj == j) {
-          p = v[jj];
-          s[jj] = -INFINITY;  // taken
-        }
-      }
+    for (int j = 0; j < EPL; ++j) {
+      const bool hit = mine && j == jw;
+      p = hit ? v[j] : p;
+      s[j] = hit ? -INFINITY : s[j];  // taken
+    }
+    if (mine) {
       idx[size_t(t) * K + k] = we;
       gate[size_t(t) * K + k] = p;
     }
