@@ -53,6 +53,11 @@ P* at(void* ws, size_t off) {
 lc_moe_status permute_core(const lc_moe_shape& s, const int32_t* idx, const WsPlan& p, void* ws,
                            int32_t* load, int32_t* offsets, int32_t* slot_row,
                            int32_t* perm_token, int32_t* ffn_cnt, hipStream_t st) {
+  if (p.nblocks == 1) {  // one token block: the three steps in one workgroup
+    LCM_LAUNCH(launch_permute_small(s, idx, load, ffn_cnt, offsets, at<MTile>(ws, p.mtiles),
+                                    at<int32_t>(ws, p.n_mtiles), p.bm, slot_row, perm_token, st));
+    return LC_MOE_OK;
+  }
   int32_t* bc = at<int32_t>(ws, p.block_counts);
   int32_t* bb = at<int32_t>(ws, p.block_base);
   LCM_LAUNCH(launch_histogram(s, idx, bc, ffn_cnt, p.nblocks, st));

@@ -219,6 +219,11 @@ hipError_t launch_histogram(const lc_moe_shape& s, const int32_t* idx, int32_t* 
 hipError_t launch_scan(const lc_moe_shape& s, const int32_t* block_counts, int nblocks,
                        int32_t* load, int32_t* offsets, int32_t* block_base, MTile* mtiles,
                        int32_t* n_mtiles, int bm, hipStream_t st);
+// Histogram, scan and scatter in one workgroup, for layers of one token block (T <= 256).
+hipError_t launch_permute_small(const lc_moe_shape& s, const int32_t* idx, int32_t* load,
+                                int32_t* ffn_cnt, int32_t* offsets, MTile* mtiles,
+                                int32_t* n_mtiles, int bm, int32_t* slot_row, int32_t* perm_token,
+                                hipStream_t st);
 // Stable scatter: slot_row [T][K], perm_token [nnz].
 hipError_t launch_scatter(const lc_moe_shape& s, const int32_t* idx, const int32_t* block_base,
                           int nblocks, int32_t* slot_row, int32_t* perm_token, hipStream_t st);

@@ -147,6 +147,105 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
+// Layers of one token block (T <= 256, decode): histogram, scan and scatter in one
+// workgroup of 1024 threads, with the counts, the wave masks and the offsets in LDS; the
+// three kernels above are each a few microseconds of mostly launch and latency at this
+// size.  The same integer rules, so the same results: token t is thread t (wave t / 64,
+// lane t % 64), its rank for expert e is popcount(mask of e in its wave, lanes below) plus
+// the picks of e by earlier waves, and its row is offsets[e] + rank.
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int E, int N, int bm,
+    int32_t* __restrict__ load, int32_t* __restrict__ ffn_cnt, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ n_mtiles, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ perm_token) {
+  __shared__ int cnt[kMaxE];
+  __shared__ unsigned long long masks[4 * kMaxN];  // [wave][expert]
+  __shared__ int off[kMaxN];
+  __shared__ int part[1024], part2[1024];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  for (int i = tid; i < 4 * N; i += 1024) masks[i] = 0ull;
+  __syncthreads();
+  const int t = tid;  // T <= 256: tokens on waves 0..3
+  if (t < T) {
+    int f = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+        atomicAdd(&cnt[e], 1);  // integer: exact whatever the order
+        if (e < N) {
+          ++f;
+          atomicOr(&masks[w * N + e], 1ull << lane);
+        }
+      }
+    }
+    if (ffn_cnt) ffn_cnt[t] = f;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) load[e] = cnt[e];
+  // exclusive scans over the N FFN experts of rows and of M-tiles (as in scan_kernel)
+  const int per = (N + 1023) / 1024;
+  int rs = 0, ms = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) {
+      rs += cnt[e];
+      ms += (cnt[e] + bm - 1) / bm;
+    }
+  }
+  part[tid] = rs;
+  part2[tid] = ms;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= o ? part[tid - o] : 0;
+    const int c = tid >= o ? part2[tid - o] : 0;
+    __syncthreads();
+    part[tid] += a;
+    part2[tid] += c;
+    __syncthreads();
+  }
+  int r = tid > 0 ? part[tid - 1] : 0;
+  int m = tid > 0 ? part2[tid - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) {
+      off[e] = r;
+      offsets[e] = r;
+      const int rows = cnt[e];
+      const int nt = (rows + bm - 1) / bm;
+      for (int j = 0; j < nt; ++j) {
+        MTile mt;
+        mt.expert = e;
+        mt.row0 = r + j * bm;
+        mt.rows = min(bm, rows - j * bm);
+        mt.first_tile = m;
+        mtiles[m + j] = mt;
+      }
+      r += rows;
+      m += nt;
+    }
+  }
+  if (tid == 1023) {
+    offsets[N] = part[1023];
+    *n_mtiles = part2[1023];
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below_lane = (1ull << lane) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      int row = -1;
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
+        int rank = __popcll(masks[w * N + e] & below_lane);
+        for (int ww = 0; ww < w; ++ww) rank += __popcll(masks[ww * N + e]);
+        row = off[e] + rank;
+        perm_token[row] = t;
+      }
+      slot_row[size_t(t) * K + k] = row;
+    }
+  }
+}
+
 // One workgroup per row; rows from offsets[N] on exit at once.
 template <typename V>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const V* __restrict__ x,
@@ -182,6 +281,15 @@ hipError_t launch_scan(const lc_moe_shape& s, const int32_t* block_counts, int n
                        int32_t* n_mtiles, int bm, hipStream_t st) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, block_counts, nblocks,
                      s.N + s.Z, s.N, load, offsets, block_base, mtiles, n_mtiles, bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_small(const lc_moe_shape& s, const int32_t* idx, int32_t* load,
+                                int32_t* ffn_cnt, int32_t* offsets, MTile* mtiles,
+                                int32_t* n_mtiles, int bm, int32_t* slot_row, int32_t* perm_token,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, s.T, s.K, s.N + s.Z, s.N,
+                     bm, load, ffn_cnt, offsets, mtiles, n_mtiles, slot_row, perm_token);
   return hipGetLastError();
 }
 
