@@ -359,8 +359,8 @@ def main():
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the layer runs on a single MI355X here and this build "
-              f"has no multi-GPU path; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py measures one GPU: the layer runs on a single MI355X and has no "
+              f"multi-GPU path; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
