@@ -195,9 +195,14 @@ constexpr int NL = (BM + BROWS) / 16;      // wave-wide loads per stage (52)
 constexpr int LPW = (NL + 7) / 8;          // load slots per wave (7)
 }
 
+// FSPLIT: for units whose K chunk fits the ring (at most NST steps: the split-K layers of
+// few tokens), the part rows are not loaded from wsplit but made here from the fp32 router
+// weight wr with the same split as router_split_kernel (so the same bits), and the split
+// kernel is not run: the layer saves its launch and the 1.5x bytes of the parts.
+template <bool FSPLIT>
 __global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, float* __restrict__ out,
-    int T, int d, int E, int chunk, int n_et, int splits, int n_units) {
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, const float* __restrict__ wr,
+    float* __restrict__ out, int T, int d, int E, int chunk, int n_et, int splits, int n_units) {
   using namespace rp;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
 
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
       if (q * 16 < rows) lmask |= 1 << i;
       const int t = r < rows ? t0 + r : t0;  // rows past T read a valid row; never stored
       p = x + size_t(t) * d;
-    } else if (q < NL) {
+    } else if (!FSPLIT && q < NL) {
       lmask |= 1 << i;
       const int br = r - BM, pp = br / BE, c = e0 + br % BE;
       p = wsplit + pp * part + size_t(c < E ? c : e0) * d;  // experts past E: a valid row
@@ -266,6 +271,43 @@ __global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
   for (int s = 0; s < npro; ++s) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) issue_one(i, s, s);
+  }
+  if constexpr (FSPLIT) {
+    // nk <= NST: every stage of the chunk is in the ring.  Group g (0..1535) of a stage is
+    // 4 weights of expert row g / 8, columns 4 * (g % 8); thread tid takes g = tid + 512 i.
+    float4 wv[NST][3];
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+#pragma unroll
+      for (int gi = 0; gi < 3; ++gi) {
+        const int g = tid + 512 * gi, er = g >> 3, c = e0 + er;
+        const int kk = kbeg + (s < nk ? s : 0) * BK + (g & 7) * 4;
+        wv[s][gi] = *reinterpret_cast<const float4*>(wr + size_t(c < E ? c : e0) * d + kk);
+      }
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      if (s >= nk) break;
+#pragma unroll
+      for (int gi = 0; gi < 3; ++gi) {
+        const int g = tid + 512 * gi, er = g >> 3, cg = g & 7;
+        bf16_t h[4], m[4], l[4];
+        split3(wv[s][gi].x, h[0], m[0], l[0]);
+        split3(wv[s][gi].y, h[1], m[1], l[1]);
+        split3(wv[s][gi].z, h[2], m[2], l[2]);
+        split3(wv[s][gi].w, h[3], m[3], l[3]);
+        const uint2 pv[3] = {make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16)),
+                             make_uint2(m[0] | (uint32_t(m[1]) << 16), m[2] | (uint32_t(m[3]) << 16)),
+                             make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16))};
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {  // part row pp*BE + er: slot of 16-byte chunk cg/2, half cg%2
+          const int r = BM + pp * BE + er;
+          *reinterpret_cast<uint2*>(smem + s * STAGE + r * RB + (((cg >> 1) ^ swz4(r)) << 4) + (cg & 1) * 8) = pv[pp];
+        }
+      }
+    }
+    LCM_WAIT_VMCNT(0);  // this wave's token rows landed
+    wait_lds_reads();   // and its part rows are written
+    block_barrier();
   }
 
   auto run = [&](auto nv_tag) {
@@ -513,16 +555,25 @@ hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const floa
   const int E = s.N + s.Z;
   if (s.dtype == LC_MOE_BF16) {
     const size_t n = size_t(E) * s.d;  // a multiple of 8
-    hipLaunchKernelGGL(router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
-                       w_router, wsplit, n);
     const RouterSplit rs = router_split(s);
     float* dst = rs.splits > 1 ? rpart : logits;
+    // split-K chunks that fit the ring: the pipelined kernel splits the weight itself
+    const bool fsplit = router_pipelined(s) && rs.chunk <= rp::NST * rp::BK;
+    if (!fsplit)
+      hipLaunchKernelGGL(router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
+                         w_router, wsplit, n);
     if (router_pipelined(s)) {
       const int n_et = (E + rp::BE - 1) / rp::BE;
       const int units = ((s.T + rp::BM - 1) / rp::BM) * n_et * rs.splits;
-      hipLaunchKernelGGL(router_logits_pipe_kernel, dim3(unsigned((units + 7) / 8 * 8)), dim3(512), 0,
-                         st, static_cast<const bf16_t*>(x), wsplit, dst, s.T, s.d, E, rs.chunk,
-                         n_et, rs.splits, units);
+      const dim3 grid(unsigned((units + 7) / 8 * 8));
+      if (fsplit)
+        hipLaunchKernelGGL(router_logits_pipe_kernel<true>, grid, dim3(512), 0, st,
+                           static_cast<const bf16_t*>(x), wsplit, w_router, dst, s.T, s.d, E, rs.chunk,
+                           n_et, rs.splits, units);
+      else
+        hipLaunchKernelGGL(router_logits_pipe_kernel<false>, grid, dim3(512), 0, st,
+                           static_cast<const bf16_t*>(x), wsplit, w_router, dst, s.T, s.d, E, rs.chunk,
+                           n_et, rs.splits, units);
     } else {
       dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM, rs.splits);
       hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
