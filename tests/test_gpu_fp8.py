@@ -158,14 +158,16 @@ def test_forward_fp8_decode_full_size_sampled(name):
     assert err <= BF16_TOL
 
 
-def test_forward_fp8_prefill_full_size_sampled():
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_forward_fp8_prefill_full_size_sampled(name):
     """The prefill layer at full size on FP8 weights, in the benchmark's launch
-    configuration: full 320-row tiles and the experts whose rows span two M-tiles.  The
-    oracle checks two tokens: one with the fewest FFN experts, and the token with the
-    fewest FFN experts among those routed to the most loaded expert (each oracle expert
-    costs seconds of CPU quantization)."""
+    configuration: full 320-row tiles and the experts whose rows span two M-tiles (the
+    skewed layer's head expert spans about a hundred).  The oracle checks two tokens: one
+    with the fewest FFN experts, and the token with the fewest FFN experts among those
+    routed to the most loaded expert (each oracle expert costs seconds of CPU
+    quantization)."""
     import mixture_experts_layer_router_amd as lm
-    wl = configs.get("prefill")
+    wl = configs.get(name)
     say(f"fp8 forward full size: {wl.description}")
     case = make_case(wl)
     q = quantize_on_gpu(case.w)

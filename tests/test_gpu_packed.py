@@ -121,7 +121,7 @@ def test_forward_packed_matches_row_major(T, d, I, N, Z, K):
     assert_pair(case, a, b)
 
 
-@pytest.mark.parametrize("name", ["decode_T64_z33", "prefill"])
+@pytest.mark.parametrize("name", ["decode_T64_z33", "prefill", "skewed"])
 def test_forward_packed_full_size_matches_row_major(name):
     wl = configs.get(name)
     say(f"packed forward full size: {wl.description}")
