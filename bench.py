@@ -161,11 +161,21 @@ def cpu_baseline(st, wl, ffn_budget_s=6.0):
     nnz.  Copying each expert's weights to the host is not timed."""
     from inputs.generate import weights_f64
     from oracle import moe as orc
+    blas_lib = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas_lib = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         blas_threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover
+        pass
     ri = st["ri"]
     x = ri.x_f64()
     wr = ri.w_router.astype(np.float64)
@@ -196,6 +206,7 @@ def cpu_baseline(st, wl, ffn_budget_s=6.0):
     t_ffn_scaled = t_ffn * nnz / max(rows, 1)
     total = t_route + t_perm + t_ffn_scaled + t_comb
     return {"value": wl.T / total, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "cpu": cpu_model, "blas": blas_lib,
             "sample": (f"fp64 numpy oracle; routing, permutation and combine over all {wl.T} tokens; "
                        f"SwiGLU FFN on the {rows} rows of the first {experts} FFN experts "
                        f"(of {nnz} FFN rows), FFN time scaled by {nnz}/{rows}; "
