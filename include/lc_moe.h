@@ -27,13 +27,19 @@
  *     LC_MOE_F32: they are fp32.  The router weight W_r, the bias b and the gates are
  *     always fp32; arithmetic accumulates in fp32 (the router logits exactly as an fp32
  *     dot product of x with W_r).
- *   - Host-side checks run before anything is enqueued.  On any error status nothing is
- *     enqueued and every output is left untouched.  Device faults surface at the
- *     caller's next synchronisation.  NaN or Inf inputs are outside the contract.
+ *   - Host-side checks (LC_MOE_E_NULLPTR, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE) run before
+ *     anything is enqueued: on those statuses nothing is enqueued and every output is left
+ *     untouched.  LC_MOE_E_DEVICE reports a launch error from the HIP runtime; kernels of
+ *     the same call launched before it may already be enqueued, so the outputs are then
+ *     undefined.  Device faults surface at the caller's next synchronisation.  NaN or Inf
+ *     inputs are outside the contract.
  *   - Results are deterministic: two calls with the same inputs give bitwise equal
  *     outputs (no floating-point atomics anywhere).
  *   - Limits: T, d, N, K, I >= 1; Z >= 0; K <= N+Z; N+Z <= 4096; N <= 2048;
- *     T*K < 2^31; d and I multiples of 8 for bf16 (4 for fp32).
+ *     d and I multiples of 8 for bf16 (4 for fp32); and every kernel launch of the shape
+ *     within the device's grid (at most 2^32 - 1 work-items along x): this needs
+ *     T*K < 2^24, and for layers with many experts' worth of tiles somewhat less.  A shape
+ *     outside these limits gives LC_MOE_E_SHAPE (lc_moe_workspace_size returns 0).
  */
 #ifndef LC_MOE_H
 #define LC_MOE_H
@@ -105,7 +111,8 @@ lc_moe_status lc_moe_route(const lc_moe_shape* shape, const void* x, const float
 
 /* Expert usage counts, the statistic a bias controller consumes (bias paragraph of the
  * same section: the bias follows recent expert usage).
- *   topk_idx       [T][K] int32       picks (values in 0..N+Z-1)
+ *   topk_idx       [T][K] int32       picks (values in 0..N+Z-1; a token may repeat an
+ *                                     expert, each pick counts)
  *   load           [N+Z] int32 (out)  number of picks of each expert; sums to T*K
  *   ffn_per_token  [T] int32 (out)    number of FFN experts (index < N) among each
  *                                     token's picks, 0..K; may be NULL */
@@ -116,12 +123,15 @@ lc_moe_status lc_moe_expert_load(const lc_moe_shape* shape, const int32_t* topk_
 /* Token permutation into expert-contiguous rows.  Zero-computation picks get no row:
  * they need no compute (section "Zero-computation experts").
  *   x            [T][d] dtype
- *   topk_idx     [T][K] int32
+ *   topk_idx     [T][K] int32        values in 0..N+Z-1; a token may pick an expert more
+ *                                    than once, and every such pick gets its own row
+ *                                    (the router's picks are always distinct; repeated
+ *                                    ones take a slower, serial ranking of their block)
  *   ffn_offsets  [N+1] int32 (out)   exclusive prefix sum of the FFN experts' loads;
  *                                    ffn_offsets[N] = nnz, the number of FFN picks
  *   perm_token   [T*K] int32 (out)   token of each row; rows of expert e are
- *                                    ffn_offsets[e]..ffn_offsets[e+1]-1, tokens
- *                                    ascending; entries from nnz on are untouched
+ *                                    ffn_offsets[e]..ffn_offsets[e+1]-1, in (token,
+ *                                    pick) order; entries from nnz on are untouched
  *   slot_row     [T][K] int32 (out)  row of pick (t,k), -1 for a zero-computation pick
  *   x_perm       [T*K][d] dtype (out) x_perm[r] = x[perm_token[r]] for r < nnz; may be NULL
  *   load         [N+Z] int32 (out)   as lc_moe_expert_load; may be NULL */
@@ -131,10 +141,14 @@ lc_moe_status lc_moe_permute(const lc_moe_shape* shape, const void* x, const int
                              size_t workspace_bytes, hipStream_t stream);
 
 /* Whole layer: route -> permute -> grouped SwiGLU FFN over the FFN picks only ->
- * combine, where the combine adds, in the order of each token's picks, g * (expert
- * output) for FFN picks and g * x_t for zero-computation picks, in fp32, rounding y
- * once to dtype (nearest even).  Intermediates (gated activations, expert outputs) are
- * stored in dtype.  One stream, no host synchronisation, capturable into a HIP graph.
+ * combine.  For each token the combine accumulates in fp32, starting from zero: first
+ * g * (expert output) of each FFN pick, in pick order (one fused multiply-add per
+ * element and pick); then, if the token has zero-computation picks, gz * x_t, where gz
+ * is the fp32 sum of their gates taken in pick order; y is rounded once to dtype
+ * (nearest even).  So the result equals the layer's sum with the identity experts'
+ * terms grouped as (sum of their gates) * x_t.  Intermediates (gated activations H,
+ * expert outputs) are stored in dtype (nearest even).  One stream, no host
+ * synchronisation, capturable into a HIP graph.
  *   x          [T][d] dtype
  *   weights    host struct of device pointers (see lc_moe_weights)
  *   y          [T][d] dtype (out)

@@ -42,6 +42,11 @@ class Workload:
     plant_frac: float = 0.0    # fraction of "easy" and of "hard" tokens planted
     plant_scale: float = 3.0
     description: str = ""
+    weight_key: tuple = None   # seed words of the expert weights (default: seed_key)
+
+    @property
+    def weight_seed_key(self) -> tuple:
+        return self.weight_key if self.weight_key is not None else self.seed_key
 
     @property
     def E(self) -> int:
@@ -86,25 +91,29 @@ def _small() -> Workload:
         description="small bf16 layer T=4096 d=2048 N=64 Z=32 K=6 I=1024")
 
 
+PREFILL_SEED = (2,)
+
+
 def _prefill() -> Workload:
     E = 768
     return Workload(
         name="prefill", T=16384, d=6144, N=512, Z=256, K=12, I=2048, dtype="bf16",
-        seed_key=(2,), expert_std=1.0 / math.sqrt(6144),
+        seed_key=PREFILL_SEED, expert_std=1.0 / math.sqrt(6144),
         bias=("uniform+shift", 0.1 / E, 1.0 / 3.0),
         description="prefill bf16 layer T=16384 d=6144 N=512 Z=256 K=12 I=2048, "
                     "mean 8 FFN experts per token")
 
 
 def decode(T: int, share_pct: int) -> Workload:
-    """Decode-step workload: the prefill layer's expert pool at T in {64,128,256}."""
+    """Decode-step workload: the prefill layer itself (same expert weights) run on a batch
+    of T in {64,128,256} tokens; its own tokens, router weights and biases."""
     E = 768
     a = 0.1 / E
     bias = ("exclude_zero", a) if share_pct == 0 else ("uniform+shift", a, share_pct / 100.0)
     return Workload(
         name=f"decode_T{T}_z{share_pct}", T=T, d=6144, N=512, Z=256, K=12, I=2048,
         dtype="bf16", seed_key=(3, T, share_pct), expert_std=1.0 / math.sqrt(6144),
-        bias=bias,
+        bias=bias, weight_key=PREFILL_SEED,
         description=f"decode bf16 layer T={T} d=6144 N=512 Z=256 K=12 I=2048, "
                     f"zero-expert share {share_pct}%")
 

@@ -159,9 +159,11 @@ def routing_inputs(wl: Workload, beta: float | None = None, resample=None) -> Ro
 def expert_weights(wl: Workload, device="cpu") -> dict:
     """W_gate [N,I,d], W_up [N,I,d], W_down [N,d,I] as torch tensors on ``device``.
 
-    Each tensor comes from one torch generator seeded from (workload, tag); experts are
-    drawn one after another (fp32 standard normal, times the workload's std, rounded to
-    the storage dtype with round-to-nearest-even).  Draws depend on the device type.
+    Each tensor comes from one torch generator seeded from (the workload's weight seed
+    words, tag); experts are drawn one after another (fp32 standard normal, times the
+    workload's std, rounded to the storage dtype with round-to-nearest-even).  Draws
+    depend on the device type.  Workloads with the same weight seed words and shapes (the
+    prefill layer and its decode steps) get the same weights.
     """
     import torch
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
@@ -170,7 +172,7 @@ def expert_weights(wl: Workload, device="cpu") -> dict:
                              (TAG_WD, "down", (wl.d, wl.I))):
         w = torch.empty((wl.N,) + shape, dtype=tdt, device=device)
         g = torch.Generator(device=device)
-        g.manual_seed(seed64(*wl.seed_key, tag))
+        g.manual_seed(seed64(*wl.weight_seed_key, tag))
         for e in range(wl.N):
             r = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
             w[e].copy_((r * wl.expert_std).to(tdt))

@@ -17,6 +17,7 @@ lc_moe_status check_shape(const lc_moe_shape* s) {
   if (static_cast<long long>(s->T) * s->K >= (1LL << 31)) return LC_MOE_E_SHAPE;
   const int vec = s->dtype == LC_MOE_BF16 ? 8 : 4;
   if (s->d % vec != 0 || s->I % vec != 0) return LC_MOE_E_SHAPE;
+  if (!grids_fit(*s)) return LC_MOE_E_SHAPE;
   return LC_MOE_OK;
 }
 

@@ -138,6 +138,37 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   return p;
 }
 
+// Every kernel launch of a shape must fit the device's grid: at most 2^32 - 1 work-items
+// along x and 65535 workgroups along y and z.  The launchers below size their grids by
+// these same formulas; shapes whose largest launch would not fit are rejected up front.
+inline bool grids_fit(const lc_moe_shape& s) {
+  typedef unsigned long long u64;
+  const u64 lim = 0xFFFFFFFFull;
+  const u64 T = u64(s.T), K = u64(s.K), E = u64(s.N) + u64(s.Z), d = u64(s.d), I = u64(s.I);
+  const bool bf = s.dtype == LC_MOE_BF16;
+  bool f = true;
+  f = f && T * K * 256 <= lim;          // gather_rows_kernel: one workgroup per pick
+  f = f && T * 256 <= lim;              // combine: one workgroup per token
+  f = f && (T + 3) / 4 * 256 <= lim;    // top-K: one wave per token
+  const WsPlan p = plan_workspace(s);
+  const u64 nn_gu = bf ? (I + 127) / 128 : (I + 63) / 64;
+  const u64 nn_d = bf ? (d + 255) / 256 : (d + 63) / 64;
+  const u64 units = u64(p.mt_max) * (nn_gu > nn_d ? nn_gu : nn_d);
+  f = f && (units + 7) / 8 * 8 * 512 <= lim;  // grouped FFN: one workgroup per work unit
+  if (bf) {
+    const RouterSplit rs = router_split(s);
+    f = f && (E * d / 4 + 255) / 256 * 256 <= lim;  // router weight split
+    if (router_pipelined(s))
+      f = f && ((T + kRouterBm - 1) / kRouterBm) * ((E + kRouterBe - 1) / kRouterBe) * u64(rs.splits) * 512 <= lim;
+    else
+      f = f && (T + 127) / 128 <= 65535 && u64(rs.splits) <= 65535;
+    f = f && (T * E + 1023) / 1024 * 256 <= lim;  // split-K sum
+  } else {
+    f = f && (T + 63) / 64 <= 65535;
+  }
+  return f;
+}
+
 // XOR swizzle of the 16-byte chunk slot for 64-byte LDS rows: the 32 rows of one MFMA
 // operand read spread over all banks.
 __host__ __device__ __forceinline__ int swz4(int r) {
@@ -256,7 +287,8 @@ hipError_t launch_pack_weights(const lc_moe_shape& s, const void* w_gate, const 
 hipError_t launch_quantize_weights(const lc_moe_shape& s, const void* w_gate, const void* w_up,
                                    const void* w_down, void* out, hipStream_t st);
 
-// y_t = sum_k g_tk * (FFN row or x_t), k ascending, fp32 accumulation.
+// y_t = (sum over the token's FFN picks, in pick order, of g * FFN row)
+//       + (sum of its zero-computation picks' gates, in pick order) * x_t, fp32 accumulation.
 hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,
                           const int32_t* slot_row, const float* gate, void* y, hipStream_t st);
 

@@ -388,8 +388,11 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
   if (FP8) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int sbase = MODE == 0 ? ((e * 2 + nb) * nrb_rows + ntile) * nkb
-                                  : (e * nrb_rows + ntile * 2 + ((wn * 64 + nb * 32) >> 7)) * nkb;
+      // MODE 1: the 256-row n-tile spans two 128-row blocks; in the last n-tile of a
+      // matrix whose rows end in its first half the second block does not exist (its rows
+      // hold zero codes), so its lanes take the last block's scales instead.
+      const int rb = MODE == 0 ? ntile : min(ntile * 2 + ((wn * 64 + nb * 32) >> 7), nrb_rows - 1);
+      const int sbase = MODE == 0 ? ((e * 2 + nb) * nrb_rows + rb) * nkb : (e * nrb_rows + rb) * nkb;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kb = h * 64 + lane;

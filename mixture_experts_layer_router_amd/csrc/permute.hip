@@ -4,11 +4,15 @@
 // "Zero-computation experts"); the load histogram is the "recent expert usage" signal
 // the bias adjustment of that section consumes.
 //
-// Order: rows of expert e are ffn_offsets[e] .. ffn_offsets[e+1]-1 with tokens ascending.
-// Tokens are cut into blocks of 256; a block's rank of token t for expert e is
+// Order: rows of expert e are ffn_offsets[e] .. ffn_offsets[e+1]-1 in (token, pick)
+// order.  Tokens are cut into blocks of 256; a block's rank of token t for expert e is
 //   (picks of e in earlier blocks) + (picks of e by earlier waves of the block)
 //   + popcount(64-lane mask of e in t's wave, lanes below t),
-// all integer, so the result is independent of thread timing.
+// all integer, so the result is independent of thread timing.  The masks hold one bit per
+// token, which ranks correctly only while a token picks an expert at most once (as the
+// router's top-K always does).  A caller's topk_idx may repeat an expert within a token:
+// the mask's atomicOr then returns the bit already set, and the block ranks its picks one
+// by one in (token, pick) order instead, so every pick still gets its own row.
 #include "common.h"
 
 namespace lcm {
@@ -112,25 +116,54 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Ranks the FFN picks of tokens t0..t1-1 one by one in (token, pick) order, run[e] holding
+// the next row of expert e; one thread, for token blocks with repeated picks.
+__device__ void scatter_serial(const int32_t* __restrict__ idx, int t0, int t1, int K, int N,
+                               int* run, int32_t* __restrict__ slot_row,
+                               int32_t* __restrict__ perm_token) {
+  for (int t = t0; t < t1; ++t)
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[size_t(t) * K + k];
+      int row = -1;
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
+        row = run[e]++;
+        perm_token[row] = t;
+      }
+      slot_row[size_t(t) * K + k] = row;
+    }
+}
+
 // 256 threads = 4 waves; wave w owns tokens b*256 + w*64 + lane.  Dynamic LDS: 4*N masks.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ block_base,
                                                       int32_t* __restrict__ slot_row,
                                                       int32_t* __restrict__ perm_token, int T,
                                                       int K, int N) {
-  extern __shared__ unsigned long long masks[];  // [4][N]
+  extern __shared__ unsigned long long masks[];  // [4][N]; reused as int run[N]
+  __shared__ int repeated;                       // a token of the block picks an expert twice
   const int tid = threadIdx.x, b = blockIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   for (int i = tid; i < 4 * N; i += 256) masks[i] = 0ull;
+  if (tid == 0) repeated = 0;
   __syncthreads();
   const int t = b * kTokBlock + tid;
   if (t < T) {
     for (int k = 0; k < K; ++k) {
       const int e = idx[size_t(t) * K + k];
-      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) atomicOr(&masks[w * N + e], 1ull << lane);
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
+        const unsigned long long bit = 1ull << lane;
+        if (atomicOr(&masks[w * N + e], bit) & bit) repeated = 1;
+      }
     }
   }
   __syncthreads();
+  if (repeated) {  // uniform over the block
+    int* run = reinterpret_cast<int*>(masks);
+    for (int e = tid; e < N; e += 256) run[e] = block_base[size_t(b) * N + e];
+    __syncthreads();
+    if (tid == 0) scatter_serial(idx, b * kTokBlock, min(T, (b + 1) * kTokBlock), K, N, run, slot_row, perm_token);
+    return;
+  }
   if (t < T) {
     const unsigned long long below_lane = (1ull << lane) - 1ull;
     for (int k = 0; k < K; ++k) {
@@ -162,9 +195,11 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   __shared__ unsigned long long masks[4 * kMaxN];  // [wave][expert]
   __shared__ int off[kMaxN];
   __shared__ int part[1024], part2[1024];
+  __shared__ int repeated;  // a token picks an expert twice: rank one by one (as scatter_kernel)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   for (int i = tid; i < 4 * N; i += 1024) masks[i] = 0ull;
+  if (tid == 0) repeated = 0;
   __syncthreads();
   const int t = tid;  // T <= 256: tokens on waves 0..3
   if (t < T) {
@@ -175,7 +210,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
         atomicAdd(&cnt[e], 1);  // integer: exact whatever the order
         if (e < N) {
           ++f;
-          atomicOr(&masks[w * N + e], 1ull << lane);
+          const unsigned long long bit = 1ull << lane;
+          if (atomicOr(&masks[w * N + e], bit) & bit) repeated = 1;
         }
       }
     }
@@ -230,6 +266,10 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     *n_mtiles = part2[1023];
   }
   __syncthreads();
+  if (repeated) {  // uniform over the workgroup
+    if (tid == 0) scatter_serial(idx, 0, T, K, N, off, slot_row, perm_token);
+    return;
+  }
   if (t < T) {
     const unsigned long long below_lane = (1ull << lane) - 1ull;
     for (int k = 0; k < K; ++k) {

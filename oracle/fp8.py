@@ -72,6 +72,38 @@ def block_exponent(amax: float) -> int:
     return k
 
 
+_BF16_CODES = None
+
+
+def bf16_code_table():
+    """e4m3_encode of every bf16 value, indexed by its 16-bit pattern (a memo of that
+    function for bf16 inputs); patterns whose value is not finite or exceeds 448 in
+    magnitude are marked False in the second array."""
+    global _BF16_CODES
+    if _BF16_CODES is None:
+        with np.errstate(invalid="ignore"):
+            vals = (np.arange(65536, dtype=np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+            ok = np.isfinite(vals) & (np.abs(vals) <= E4M3_MAX)
+        codes = np.zeros(65536, np.uint8)
+        codes[ok] = e4m3_encode(vals[ok])
+        _BF16_CODES = (codes, ok)
+    return _BF16_CODES
+
+
+def encode_scaled(q) -> np.ndarray:
+    """e4m3_encode(q); when every q is a bf16 value (bf16 weights over a power-of-two
+    scale always are), through the memo table of bf16_code_table."""
+    q = np.asarray(q, np.float64)
+    q32 = q.astype(np.float32)
+    bits = q32.view(np.uint32)
+    if np.array_equal(q32.astype(np.float64), q) and not np.any(bits & np.uint32(0xFFFF)):
+        codes, ok = bf16_code_table()
+        pat = bits >> np.uint32(16)
+        if np.all(ok[pat]):
+            return codes[pat]
+    return e4m3_encode(q)
+
+
 def quantize(w):
     """Block-FP8 quantization of one matrix w [rows][cols] (values exact in fp64):
     returns (codes uint8 [rows][cols], k int [ceil(rows/128)][ceil(cols/128)])."""
@@ -79,16 +111,21 @@ def quantize(w):
     R, C = w.shape
     nrb, ncb = -(-R // BLOCK), -(-C // BLOCK)
     pad = np.zeros((nrb * BLOCK, ncb * BLOCK))
-    pad[:R, :C] = np.abs(w)
-    amax = pad.reshape(nrb, BLOCK, ncb, BLOCK).max(axis=(1, 3))
+    pad[:R, :C] = w
+    blocks = pad.reshape(nrb, BLOCK, ncb, BLOCK)
+    amax = np.abs(blocks).max(axis=(1, 3))
     ks = np.array([[block_exponent(float(a)) for a in row] for row in amax], np.int64)
-    scale = np.repeat(np.repeat(2.0 ** ks, BLOCK, axis=0), BLOCK, axis=1)[:R, :C]
-    return e4m3_encode(w / scale), ks
+    q = (blocks / (2.0 ** ks)[:, None, :, None]).reshape(nrb * BLOCK, ncb * BLOCK)[:R, :C]
+    return encode_scaled(q), ks
 
 
 def dequantize(codes, ks):
     """code * 2^k per element (fp64; exact)."""
     codes = np.asarray(codes)
     R, C = codes.shape
-    scale = np.repeat(np.repeat(2.0 ** np.asarray(ks, np.float64), BLOCK, axis=0), BLOCK, axis=1)[:R, :C]
-    return E4M3_TABLE[codes] * scale
+    ks = np.asarray(ks, np.float64)
+    nrb, ncb = ks.shape
+    pad = np.zeros((nrb * BLOCK, ncb * BLOCK))
+    pad[:R, :C] = E4M3_TABLE[codes]
+    out = pad.reshape(nrb, BLOCK, ncb, BLOCK) * (2.0 ** ks)[:, None, :, None]
+    return out.reshape(nrb * BLOCK, ncb * BLOCK)[:R, :C]

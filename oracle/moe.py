@@ -22,7 +22,9 @@ Readings where the pages are silent:
     fp32 scores, the GPU kernel's precision: p is rounded to fp32 and b (fp32) is added
     in fp32; everything else here is fp64;
   * top-K output order is (s descending, index ascending);
-  * the expert permutation lists each FFN expert's tokens in ascending token order.
+  * the expert permutation lists each FFN expert's picks in (token, pick) order, i.e.
+    ascending token order (a token picking an expert twice, which the router never does,
+    would get two consecutive rows).
 
 Expert weights are given per expert through ``experts(e) -> (W_gate[I,d], W_up[I,d],
 W_down[d,I])`` in fp64, so a caller can stream them one expert at a time.
@@ -73,7 +75,7 @@ def permute(idx: np.ndarray, N: int):
     """Expert-contiguous order of the FFN picks.
 
     Returns offsets [N+1] (exclusive prefix sum of the FFN experts' loads),
-    perm_token [nnz] (the token of each row; ascending within each expert) and
+    perm_token [nnz] (the token of each row; (token, pick) order within each expert) and
     slot_row [T,K] (row of pick (t,k), -1 for a zero-computation pick).
     """
     idx = np.asarray(idx)
@@ -113,29 +115,58 @@ def combine(x, y_perm, idx, gate, slot_row, N):
     return y
 
 
+def zero_gate_sum(idx, gate, N):
+    """Per token, the sum of the gates of its zero-computation picks (their experts all
+    return x_t, so together they add this sum times x_t)."""
+    return (np.asarray(gate, np.float64) * (np.asarray(idx) >= N)).sum(axis=1)
+
+
 def moe_forward(x, w_router, bias, experts, N, K, tokens=None):
     """Whole layer forward in fp64.
 
     x [T,d] fp64, W_r [E,d], b [E]; ``experts(e)`` returns fp64 (W_gate, W_up, W_down)
     of FFN expert e.  With ``tokens`` given, only those rows are routed and combined
     (each token's result depends on its own row only).
-    Returns dict(idx, gate, y, load, ffn_count, offsets, perm_token, slot_row).
+    Returns dict(idx, gate, y, y_ffn, gz, load, ffn_count, offsets, perm_token, slot_row):
+    y_ffn is the FFN picks' part of y (the zero picks' part is gz * x, gz = zero_gate_sum).
     """
-    x = np.asarray(x, np.float64)
-    if tokens is not None:
-        x = x[np.asarray(tokens)]
-    E = w_router.shape[0]
-    idx, gate, _ = route(x, w_router, bias, K)
-    offsets, perm_token, slot_row = permute(idx, N)
-    y_perm = np.zeros((perm_token.size, x.shape[1]))
+    return moe_forward_batches([dict(x=x, w_router=w_router, bias=bias, K=K, tokens=tokens)],
+                               experts, N)[0]
+
+
+def moe_forward_batches(batches, experts, N):
+    """moe_forward of several token batches through one layer's experts (for instance a
+    prefill batch and decode batches of the same layer), with one pass over the experts:
+    ``experts(e)`` is called once for every expert that any batch routes a token to.
+    batches: list of dict(x, w_router, bias, K, tokens=None); returns one moe_forward result
+    per batch, each equal to moe_forward on that batch alone."""
+    prep = []
+    for b in batches:
+        x = np.asarray(b["x"], np.float64)
+        if b.get("tokens") is not None:
+            x = x[np.asarray(b["tokens"])]
+        idx, gate, _ = route(x, b["w_router"], b["bias"], b["K"])
+        offsets, perm_token, slot_row = permute(idx, N)
+        prep.append(dict(x=x, E=b["w_router"].shape[0], idx=idx, gate=gate, offsets=offsets,
+                         perm_token=perm_token, slot_row=slot_row,
+                         y_perm=np.zeros((perm_token.size, x.shape[1]))))
     for e in range(N):
-        r0, r1 = offsets[e], offsets[e + 1]
-        if r1 > r0:
-            wg, wu, wd = experts(e)
-            y_perm[r0:r1] = swiglu_expert(x[perm_token[r0:r1]], wg, wu, wd)
-    y = combine(x, y_perm, idx, gate, slot_row, N)
-    return dict(idx=idx, gate=gate, y=y, load=expert_load(idx, E), ffn_count=ffn_count(idx, N),
-                offsets=offsets, perm_token=perm_token, slot_row=slot_row)
+        if all(q["offsets"][e + 1] == q["offsets"][e] for q in prep):
+            continue
+        wg, wu, wd = experts(e)
+        for q in prep:
+            r0, r1 = q["offsets"][e], q["offsets"][e + 1]
+            if r1 > r0:
+                q["y_perm"][r0:r1] = swiglu_expert(q["x"][q["perm_token"][r0:r1]], wg, wu, wd)
+    out = []
+    for q in prep:
+        x, idx, gate, slot_row = q["x"], q["idx"], q["gate"], q["slot_row"]
+        y = combine(x, q["y_perm"], idx, gate, slot_row, N)
+        y_ffn = combine(np.zeros_like(x), q["y_perm"], idx, gate, slot_row, N)
+        out.append(dict(idx=idx, gate=gate, y=y, y_ffn=y_ffn, gz=zero_gate_sum(idx, gate, N),
+                        load=expert_load(idx, q["E"]), ffn_count=ffn_count(idx, N),
+                        offsets=q["offsets"], perm_token=q["perm_token"], slot_row=slot_row))
+    return out
 
 
 def selection_margin_ok(p: np.ndarray, bias: np.ndarray, K: int, rel: float = 1e-4,

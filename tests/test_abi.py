@@ -51,6 +51,10 @@ def test_workspace_size():
         args.update(kw)
         assert lm.lc_moe_workspace_size(lm.make_shape(**args)) == 0, kw
     assert lm.lc_moe_workspace_size(lm.make_shape(T=64, d=132, N=8, Z=0, K=8, I=4, dtype=lm.F32)) > 0
+    # grid limit: one workgroup of 256 work-items per pick in lc_moe_permute's row gather
+    # needs T*K*256 <= 2^32 - 1
+    assert lm.lc_moe_workspace_size(lm.make_shape((1 << 21) - 1, 128, 8, 4, 8, 256, lm.BF16)) > 0
+    assert lm.lc_moe_workspace_size(lm.make_shape(1 << 21, 128, 8, 4, 8, 256, lm.BF16)) == 0
 
 
 P = 1 << 20           # fake, 16-byte aligned device addresses: validation never dereferences
@@ -165,3 +169,38 @@ def test_forward_weight_format_validation():
     mis = lm.Weights(P, P, None, None, None, None, MIS)
     assert L.lc_moe_forward(sp, P, ctypes.byref(mis), P, None, None, None, P, nb, None) == 4
 
+
+
+HIP_MAPS = r"""
+import sys
+sys.path.insert(0, {root!r})
+{first}
+paths = set()
+for line in open('/proc/self/maps'):
+    f = line.split()
+    if len(f) >= 6 and 'libamdhip64' in f[-1]:
+        paths.add(f[-1])
+print(len(paths))
+"""
+
+
+def _hip_runtimes(first):
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = HIP_MAPS.format(root=root, first=first)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd="/tmp")
+    assert r.returncode == 0, r.stderr[-2000:]
+    return int(r.stdout.strip().splitlines()[-1])
+
+
+def test_binding_loads_one_hip_runtime():
+    """torch's wheel carries its own HIP runtime under the same soname as the system one
+    liblc_moe.so links to; a process that maps both crashed in a GPU run.  The binding
+    imports torch before opening the library, so the library binds to the runtime already
+    loaded and the process maps exactly one.  The other order (library first) maps two,
+    which shows the check can fail."""
+    assert _hip_runtimes("import mixture_experts_layer_router_amd as lm; lm.lib()") == 1
+    lib = os.path.join(os.path.dirname(os.path.abspath(lm.__file__)), "liblc_moe.so")
+    wrong = f"import ctypes; ctypes.CDLL({lib!r}); import torch"
+    assert _hip_runtimes(wrong) == 2

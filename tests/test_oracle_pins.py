@@ -217,6 +217,52 @@ def test_token_subset_equals_full_rows():
     assert (sub["idx"] == full["idx"][[3, 17, 29]]).all()
 
 
+def test_batches_share_one_pass_over_the_experts():
+    """moe_forward_batches equals moe_forward on each batch alone (bitwise: the same steps
+    per batch), fetches each expert's weights once, and splits y into the FFN part and
+    the zero picks' gate sum times x."""
+    c = micro(63, T=40, N=5, Z=3, K=3, bias_scale=0.2)
+    d = micro(64, T=7, N=5, Z=3, K=3, bias_scale=0.2)
+    e = micro(65, T=20, N=5, Z=3, K=3, bias_scale=0.2)
+    W = (c["w_gate"], c["w_up"], c["w_down"])          # one layer's experts for all batches
+    calls = []
+
+    def experts(k):
+        calls.append(k)
+        return W[0][k], W[1][k], W[2][k]
+
+    batches = [dict(x=b["x"], w_router=b["w_router"], bias=b["bias"], K=3) for b in (c, d)]
+    batches.append(dict(x=e["x"], w_router=e["w_router"], bias=e["bias"], K=3, tokens=[0, 5, 19]))
+    outs = orc.moe_forward_batches(batches, experts, 5)
+    assert sorted(calls) == sorted(set(calls))            # once per expert
+    for b, out in zip(batches, outs):
+        one = orc.moe_forward(b["x"], b["w_router"], b["bias"], lambda k: (W[0][k], W[1][k], W[2][k]), 5, 3,
+                              tokens=b.get("tokens"))
+        for key in ("idx", "gate", "y", "y_ffn", "gz", "load", "offsets", "perm_token", "slot_row"):
+            np.testing.assert_array_equal(out[key], one[key], err_msg=key)
+        x = np.asarray(b["x"])[b["tokens"]] if b.get("tokens") is not None else np.asarray(b["x"])
+        np.testing.assert_allclose(out["y"], out["y_ffn"] + out["gz"][:, None] * x, rtol=1e-13, atol=1e-15)
+        zg = np.where(out["idx"] >= 5, out["gate"], 0.0).sum(axis=1)
+        np.testing.assert_allclose(out["gz"], zg, rtol=1e-15)
+    # and against the scalar brute force with that layer's experts
+    bidx, _, by = bruteforce.forward(np.asarray(d["x"]).tolist(), np.asarray(d["w_router"]).tolist(),
+                                     np.asarray(d["bias"]).tolist(), W[0].tolist(), W[1].tolist(),
+                                     W[2].tolist(), 5, 3)
+    assert outs[1]["idx"].tolist() == bidx
+    np.testing.assert_allclose(outs[1]["y"], by, rtol=1e-12, atol=1e-14)
+
+
+def test_permute_repeated_picks_get_one_row_each():
+    """A caller's picks may repeat an expert within a token: every (token, pick) gets its
+    own row, in (token, pick) order, and the load counts each pick."""
+    idx = np.array([[2, 0, 2], [1, 7, 1], [2, 2, 2], [0, 5, 6]])
+    offsets, perm_token, slot_row = orc.permute(idx, 5)
+    assert offsets.tolist() == [0, 2, 4, 9, 9, 9]
+    assert perm_token.tolist() == [0, 3, 1, 1, 0, 0, 2, 2, 2]
+    assert slot_row.tolist() == [[4, 0, 5], [2, -1, 3], [6, 7, 8], [1, -1, -1]]
+    assert orc.expert_load(idx, 8).tolist() == [2, 2, 5, 0, 0, 1, 1, 1]
+
+
 # ---- the pins have teeth: plant mistakes in (a copy of) the oracle ------------------------
 
 def _mutant_checks(monkeypatch, name, fn):
