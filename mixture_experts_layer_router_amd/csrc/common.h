@@ -94,6 +94,14 @@ inline RouterSplit router_split(const lc_moe_shape& s) {
   return r;
 }
 
+// The pipelined router's ring holds 3 stages of 32 K columns.  A split-K chunk of at most
+// that many columns is loaded as fp32 and split into its bf16 parts inside the kernel, so
+// the layer needs no separate split of the router weight (nor its workspace region).
+constexpr int kRouterRingK = 3 * 32;
+inline bool router_fused_split(const lc_moe_shape& s) {
+  return router_pipelined(s) && router_split(s).chunk <= kRouterRingK;
+}
+
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsPlan {
   size_t logits, wsplit, rpart, idx, gate, block_counts, block_base, load, offsets, mtiles,
@@ -119,8 +127,9 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   p.logits = take(T * E * 4);
   const RouterSplit rs = router_split(s);
-  // the fp32 router weight as three bf16 parts (bf16 layers)
-  p.wsplit = take(s.dtype == LC_MOE_BF16 ? 3 * E * size_t(s.d) * 2 : 0);
+  // the fp32 router weight as three bf16 parts (bf16 layers whose router does not split it
+  // in the kernel)
+  p.wsplit = take(s.dtype == LC_MOE_BF16 && !router_fused_split(s) ? 3 * E * size_t(s.d) * 2 : 0);
   p.rpart = take(rs.splits > 1 ? size_t(rs.splits) * T * E * 4 : 0);
   p.idx = take(tk * 4);
   p.gate = take(tk * 4);

@@ -188,7 +188,6 @@ __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
 namespace rp {
 constexpr int BM = kRouterBm, BE = kRouterBe, NP = 3, BK = 32, RB = BK * 2;
 constexpr int BROWS = NP * BE;             // 576 part rows
-constexpr int A_BYTES = BM * RB;           // 16 KB
 constexpr int STAGE = (BM + BROWS) * RB;   // 52 KB
 constexpr int NST = 3;                     // ring stages
 constexpr int NL = (BM + BROWS) / 16;      // wave-wide loads per stage (52)
@@ -558,7 +557,8 @@ hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const floa
     const RouterSplit rs = router_split(s);
     float* dst = rs.splits > 1 ? rpart : logits;
     // split-K chunks that fit the ring: the pipelined kernel splits the weight itself
-    const bool fsplit = router_pipelined(s) && rs.chunk <= rp::NST * rp::BK;
+    const bool fsplit = router_fused_split(s);
+    static_assert(rp::NST * rp::BK == kRouterRingK, "ring depth of the pipelined router");
     if (!fsplit)
       hipLaunchKernelGGL(router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
                          w_router, wsplit, n);
