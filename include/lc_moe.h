@@ -21,8 +21,10 @@
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers, row-major and contiguous, aligned to 16
  *     bytes; the caller owns them and keeps them alive until the stream work completes.
- *     The library allocates no device memory, never synchronises the stream, keeps no
- *     pointer after return and holds no mutable global state.
+ *     The library allocates no device memory, never synchronises the stream and keeps no
+ *     pointer after return.  Its only mutable global state is that of
+ *     lc_moe_forward_noalloc: one static workspace array per GPU and a cache of its
+ *     device addresses.
  *   - dtype LC_MOE_BF16: x, the three expert weight tensors and y are bf16;
  *     LC_MOE_F32: they are fp32.  The router weight W_r, the bias b and the gates are
  *     always fp32; arithmetic accumulates in fp32 (the router logits exactly as an fp32
@@ -168,6 +170,24 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
                                     float* topk_gate, int32_t* load, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* stage_events);
+
+/* lc_moe_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments as
+ * lc_moe_forward without the workspace, same kernels, so the same results bit for bit.
+ * The workspace is a file-scope device array of LC_MOE_STATIC_WORKSPACE_BYTES, one per
+ * GPU, held from the library's load until the process ends; this entry point takes its
+ * address (hipGetSymbolAddress) on its first call on each device and calls no allocating
+ * routine.  Shapes whose lc_moe_workspace_size exceeds the array give LC_MOE_E_WORKSPACE
+ * with nothing enqueued (every decode-sized layer fits: the 768-expert, d=6144, I=2048
+ * layer needs 97 MB at T=256).  Nothing in the array needs to start at zero: every region
+ * a kernel reads was written earlier in the same call.  All calls on one GPU share the
+ * array, and it keeps the last call's contents: calls that overlap in time on one GPU (on
+ * different streams, or from different host threads) race and give undefined results;
+ * the caller must order them. */
+#define LC_MOE_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+lc_moe_status lc_moe_forward_noalloc(const lc_moe_shape* shape, const void* x,
+                                     const lc_moe_weights* weights, void* y, int32_t* topk_idx,
+                                     float* topk_gate, int32_t* load, hipStream_t stream);
 
 /* Block-FP8 expert weights.  The pages quantize with the fine-grained block scheme of
  * DeepSeek-V3 (LongCat-Flash article, section "System-level optimisation", quantization

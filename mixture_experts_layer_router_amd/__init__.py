@@ -7,7 +7,8 @@ device memory and streams.  The library is opened on first use and a missing bui
 (``python -m mixture_experts_layer_router_amd.build``); there is no fallback path.
 
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
-``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_bias_update``,
+``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_forward_noalloc``,
+``lc_moe_bias_update``,
 ``lc_moe_quantize_weights``, ``lc_moe_fp8_weights_size``, ``lc_moe_pack_weights``,
 ``lc_moe_packed_weights_size``, ``lc_moe_workspace_size``); ``route``, ``expert_load``,
 ``permute``, ``forward``, ``bias_update``, ``quantize_weights`` and ``pack_weights``
@@ -59,6 +60,8 @@ _SIG = {
                                       _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_forward_staged": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights),
                                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "lc_moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights), _vp,
+                                              _vp, _vp, _vp, _vp]),
     "lc_moe_fp8_weights_size": (_sz, [ctypes.POINTER(Shape)]),
     "lc_moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_packed_weights_size": (_sz, [ctypes.POINTER(Shape)]),
@@ -191,6 +194,15 @@ def lc_moe_forward(shape, x, weights: Weights, y, topk_idx, topk_gate, load, wor
     _check(lib().lc_moe_forward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
                                _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _ptr(workspace),
                                _nbytes(workspace), _stream(stream)), "lc_moe_forward")
+
+
+STATIC_WORKSPACE_BYTES = 128 << 20   # LC_MOE_STATIC_WORKSPACE_BYTES
+
+
+def lc_moe_forward_noalloc(shape, x, weights: Weights, y, topk_idx, topk_gate, load, stream=None):
+    _check(lib().lc_moe_forward_noalloc(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(y),
+                                       _ptr(topk_idx), _ptr(topk_gate), _ptr(load), _stream(stream)),
+           "lc_moe_forward_noalloc")
 
 
 def lc_moe_forward_staged(shape, x, weights: Weights, y, topk_idx, topk_gate, load, workspace,

@@ -1,10 +1,37 @@
 // C-ABI entry points of lc_moe: argument checks, workspace carving, launch sequence.
 // The layer definition and every argument's meaning are documented in include/lc_moe.h.
+#include <mutex>
+
 #include "common.h"
 
 using namespace lcm;
 
+// Workspace of lc_moe_forward_noalloc: one copy per GPU, allocated by the runtime with the
+// library's code object.  In host code `scratch` is a stand-in symbol, not a device
+// address: host code only ever uses the address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) unsigned char scratch[LC_MOE_STATIC_WORKSPACE_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch`, looked up once per device with the device
+// current (each GPU holds its own copy at its own address).
+lc_moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LC_MOE_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LC_MOE_E_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LC_MOE_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -275,6 +302,17 @@ lc_moe_status lc_moe_bias_update(const lc_moe_shape* shape, const lc_moe_pid* ga
                                 gains->ki, gains->kd, load, target, bias, integral, prev_err,
                                 stream));
   return LC_MOE_OK;
+}
+
+lc_moe_status lc_moe_forward_noalloc(const lc_moe_shape* shape, const void* x,
+                                     const lc_moe_weights* weights, void* y, int32_t* topk_idx,
+                                     float* topk_gate, int32_t* load, hipStream_t stream) {
+  LCM_CHECK(check_shape(shape));
+  if (plan_workspace(*shape).total > LC_MOE_STATIC_WORKSPACE_BYTES) return LC_MOE_E_WORKSPACE;
+  void* ws = nullptr;
+  LCM_CHECK(scratch_of_current_device(&ws));
+  return lc_moe_forward_staged(shape, x, weights, y, topk_idx, topk_gate, load, ws,
+                               LC_MOE_STATIC_WORKSPACE_BYTES, stream, nullptr);
 }
 
 lc_moe_status lc_moe_forward(const lc_moe_shape* shape, const void* x,

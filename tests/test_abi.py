@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -204,3 +204,18 @@ def test_binding_loads_one_hip_runtime():
     lib = os.path.join(os.path.dirname(os.path.abspath(lm.__file__)), "liblc_moe.so")
     wrong = f"import ctypes; ctypes.CDLL({lib!r}); import torch"
     assert _hip_runtimes(wrong) == 2
+
+
+def test_forward_noalloc_validation():
+    """The allocation-free forward rejects bad shapes and shapes whose workspace exceeds its
+    static array on the host, before it looks up the array or enqueues anything."""
+    L = lm.lib()
+    w = lm.Weights(P, P, P, P, P)
+    bad = lm.make_shape(64, 128, 8, 4, 13, 256, lm.BF16)
+    assert L.lc_moe_forward_noalloc(ctypes.byref(bad), P, ctypes.byref(w), P, None, None, None, None) == 2
+    prefill = lm.make_shape(16384, 6144, 512, 256, 12, 2048, lm.BF16)
+    assert lm.lc_moe_workspace_size(prefill) > lm.STATIC_WORKSPACE_BYTES
+    assert L.lc_moe_forward_noalloc(ctypes.byref(prefill), P, ctypes.byref(w), P, None, None, None, None) == 5
+    for T in (64, 128, 256):   # every decode batch of the prefill layer fits
+        assert lm.lc_moe_workspace_size(lm.make_shape(T, 6144, 512, 256, 12, 2048, lm.BF16)) <= \
+            lm.STATIC_WORKSPACE_BYTES
