@@ -1,7 +1,8 @@
 """Benchmark of the zero-computation-expert MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--no-decode] [--no-cpu-baseline] [--calib-copy]
+                    [--no-decode] [--no-extra] [--no-cpu-baseline] [--no-packed]
+                    [--no-overlap] [--calib-copy]
 
 One step = one lc_moe_forward (router, permutation, grouped SwiGLU FFN, combine) over the
 workload's resident inputs.  Prints ONE JSON line.  value = tokens/s of the whole layer
@@ -10,14 +11,18 @@ lc_moe_forward_staged on the launch stream inside the timed region; step_ms_perc
 gives p10/p50/p90 of the timed steps' spans (first to last stage event of each step).
 
 roofline: the dominant kernel is the gate/up grouped GEMM (ffn_bf16_pipe_kernel<0>: two
-thirds of the FFN FLOPs and weight bytes).  At this shape its HBM floor (algorithmic bytes
-/ 8 TB/s) lies above its MFMA floor (FLOPs / 2.5 PFLOP/s), so the bound is HBM: achieved =
-algorithmic bytes per launch (gate and up weights of every touched expert, 2*I*d*2 bytes
-each, plus d*2 bytes of x read and I*2 bytes of H written per FFN pick) over the mean
-event-timed launch duration.  The MFMA fraction (4*d*I FLOPs per FFN pick) is reported
-beside it.  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
-(scaled by a plain-copy calibration), read from the committed profile summary and dropped
-(null) when the kernel source no longer matches the one the counters were taken on.
+thirds of the FFN FLOPs and weight bytes).  Its algorithmic work per launch: 4*d*I FLOPs
+per FFN pick, and as bytes the gate and up weights of every touched expert (2*I*d*2 each)
+plus x read once (T*d*2); the per-pick row gathers and the H rows it writes are the
+implementation's (implementation_bytes).  The bound is the larger of the two floors
+(bytes / 8 TB/s, FLOPs / 2.5 PFLOP/s): HBM at the prefill shape, MFMA for the skewed
+layer.  achieved = algorithmic bytes (or FLOPs) per launch over the mean event-timed
+launch duration; profile_frac is the same over the mean duration of the committed
+rocprofv3 kernel trace of that workload, while the kernel source still matches it.
+traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by
+a plain-copy calibration), read from the committed profile summary and dropped (null)
+when the kernel source no longer matches the one the counters were taken on.
+small, skewed: the other two bf16 layers, each with its own stage times and roofline.
 decode: the decode-shaped layer (T in 64/128/256, zero-expert share 0/33/66%); the FFN
 (gate/up + down) is bound by streaming the weights of the experts that received at least
 one token; reported against the HBM peak.  Each decode layer is also captured into a HIP
@@ -46,6 +51,9 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_gate_up_prefill_T16384_hbm_traffic.txt")
+TRACE_PROFILES = {"prefill": os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_prefill_T16384_kernel_trace.txt"),
+                  "skewed": os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_skewed_T32768_kernel_trace.txt")}
+GATE_UP_KERNEL = "lcm::ffn_bf16_pipe_kernel<0, false, false>"
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_router_amd", "csrc", f)
                   for f in ("ffn.hip", "common.h", "lds_dma.h")]
 METRIC = "MoE-layer tokens/s and % of bf16 MFMA peak (prefill) / % HBM peak (decode)"
@@ -64,21 +72,83 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter summary, or None when the
-    summary is for another workload or another version of the kernel source."""
+def profile_fields(path):
+    """The machine-read `key: value` lines of a committed profile summary ({} if absent)."""
+    kv = {}
     try:
-        kv = {}
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(path) as fh:
             for line in fh:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return kv
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None when the
+    summary is for another workload or another version of the kernel source."""
+    kv = profile_fields(TRAFFIC_PROFILE)
+    try:
         if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
             return None
         return float(kv["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except (KeyError, ValueError):
         return None
+
+
+def profiled_gate_up_us(workload):
+    """Mean gate/up launch duration (us) in the committed rocprofv3 kernel trace of this
+    workload, or None when there is none or the kernel source has changed since."""
+    kv = profile_fields(TRACE_PROFILES.get(workload, ""))
+    try:
+        if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["gate_up_avg_us"])
+    except (KeyError, ValueError):
+        return None
+
+
+def layer_measures(wl, st, total, stages, steps):
+    """Stage times, FFN rates and the gate/up roofline of one timed run of a layer."""
+    load = st["outs"]["load"].cpu().numpy()
+    nnz = int(load[:wl.N].sum())
+    touched = int((load[:wl.N] > 0).sum())
+    st_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    gu_flops = 4.0 * wl.d * wl.I * nnz
+    dn_flops = 2.0 * wl.d * wl.I * nnz
+    gu_bytes = touched * 2.0 * wl.I * wl.d * 2 + wl.T * wl.d * 2.0
+    impl_bytes = nnz * (wl.d + wl.I) * 2.0 - wl.T * wl.d * 2.0
+    hbm_floor = gu_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    mfma_floor = gu_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    launch = st_ms["gate_up"]
+    gu_gbs = gu_bytes / (launch * 1e-3) / 1e9
+    gu_tflops = gu_flops / (launch * 1e-3) / 1e12
+    bound = "hbm" if hbm_floor >= mfma_floor else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = gu_gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = gu_tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    prof_us = profiled_gate_up_us(wl.name)
+    prof_frac = None
+    if prof_us:
+        work = gu_bytes / 1e9 if bound == "hbm" else gu_flops / 1e12
+        prof_frac = work / (prof_us * 1e-6) / peak
+    ffn_ms = st_ms["gate_up"] + st_ms["down"]
+    ffn_tflops = (gu_flops + dn_flops) / (ffn_ms * 1e-3) / 1e12
+    wbytes = touched * 3 * wl.I * wl.d * 2
+    roof = {"bound": bound, "kernel": GATE_UP_KERNEL + " (gate/up + SwiGLU)", "achieved": ach, "peak": peak,
+            "unit": unit, "frac": ach / peak, "traffic": measured_traffic(wl.name),
+            "algorithmic_bytes": gu_bytes, "implementation_bytes": impl_bytes, "flops_per_launch": gu_flops,
+            "hbm_GBps": gu_gbs, "hbm_frac": gu_gbs / HBM_PEAK_GBS,
+            "mfma_tflops": gu_tflops, "mfma_frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_floor_ms": hbm_floor, "mfma_floor_ms": mfma_floor, "launch_ms": launch,
+            "profile_launch_us": prof_us, "profile_frac": prof_frac}
+    ffn = {"rows": nnz, "touched_experts": touched, "ms": ffn_ms, "TFLOPs": ffn_tflops,
+           "mfma_frac": ffn_tflops / MFMA_BF16_PEAK_TFLOPS, "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9}
+    return {"ms_per_step": total / steps, "tokens_per_s": wl.T * steps / (total * 1e-3), "stages_ms": st_ms,
+            "roofline": roof, "ffn": ffn}
 
 
 def setup(wl, dev):
@@ -368,6 +438,7 @@ def main():
                          "row-major runs, which a per-kernel profile would then mix)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the dense-FFN-beside-the-layer two-stream measurement")
+    ap.add_argument("--no-extra", action="store_true", help="skip the small and skewed layers")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -388,21 +459,14 @@ def main():
     total, stages = run_steps(lm, st, args.steps, args.warmup)
     ms = total / args.steps
     step_pct = {f"p{q}": float(np.percentile(st["step_ms"], q)) for q in (10, 50, 90)}
-    load = st["outs"]["load"].cpu().numpy()
-    nnz = int(load[:wl.N].sum())
-    touched = int((load[:wl.N] > 0).sum())
-    st_ms = {k: float(np.mean(v)) for k, v in stages.items()}
-    gu_flops = 4.0 * wl.d * wl.I * nnz
-    dn_flops = 2.0 * wl.d * wl.I * nnz
-    gu_bytes = touched * 2.0 * wl.I * wl.d * 2 + nnz * (wl.d + wl.I) * 2.0
-    gu_gbs = gu_bytes / (st_ms["gate_up"] * 1e-3) / 1e9
-    gu_tflops = gu_flops / (st_ms["gate_up"] * 1e-3) / 1e12
-    ffn_ms = st_ms["gate_up"] + st_ms["down"]
-    ffn_tflops = (gu_flops + dn_flops) / (ffn_ms * 1e-3) / 1e12
-    wbytes = touched * 3 * wl.I * wl.d * 2
+    m = layer_measures(wl, st, total, stages, args.steps)
+    st_ms, roof, ffn = m["stages_ms"], m["roofline"], m["ffn"]
+    touched, nnz = ffn["touched_experts"], ffn["rows"]
+    gu_flops, gu_bytes = roof["flops_per_launch"], roof["algorithmic_bytes"]
     log(f"{ms:.3f} ms/step; stages {json.dumps({k: round(v, 4) for k, v in st_ms.items()})}")
-    log(f"gate_up {gu_tflops:.0f} TFLOP/s ({gu_tflops / MFMA_BF16_PEAK_TFLOPS:.1%}); FFN {ffn_tflops:.0f} "
-        f"TFLOP/s ({ffn_tflops / MFMA_BF16_PEAK_TFLOPS:.1%}); weights {wbytes / ffn_ms / 1e6:.0f} GB/s")
+    log(f"gate_up {roof['mfma_tflops']:.0f} TFLOP/s ({roof['mfma_frac']:.1%}), {roof['hbm_GBps']:.0f} GB/s "
+        f"({roof['hbm_frac']:.1%}); FFN {ffn['TFLOPs']:.0f} TFLOP/s ({ffn['mfma_frac']:.1%}); "
+        f"weights {ffn['weight_GBps']:.0f} GB/s")
 
     if args.calib_copy:
         a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
@@ -419,17 +483,8 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": wl.description, "T": wl.T, "d": wl.d, "N": wl.N, "Z": wl.Z,
                    "K": wl.K, "I": wl.I, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "lcm::ffn_bf16_pipe_kernel<0, false, false> (gate/up + SwiGLU)",
-                     "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
-                     "algorithmic_bytes": gu_bytes, "flops_per_launch": gu_flops,
-                     "mfma_tflops": gu_tflops, "mfma_frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "hbm_floor_ms": gu_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
-                     "mfma_floor_ms": gu_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3,
-                     "launch_ms": st_ms["gate_up"]},
-        "ffn": {"rows": nnz, "touched_experts": touched, "ms": ffn_ms, "TFLOPs": ffn_tflops,
-                "mfma_frac": ffn_tflops / MFMA_BF16_PEAK_TFLOPS,
-                "weight_GBps": wbytes / (ffn_ms * 1e-3) / 1e9},
+        "roofline": roof,
+        "ffn": ffn,
         "stages_ms": st_ms,
         "step_ms_percentiles": step_pct,
     }
@@ -448,7 +503,7 @@ def main():
     use_fp8(lm, st)
     total8, stages8 = run_steps(lm, st, args.steps, args.warmup)
     st8 = {k: float(np.mean(v)) for k, v in stages8.items()}
-    gu8_bytes = touched * 2.0 * wl.I * wl.d + nnz * (wl.d + wl.I) * 2.0
+    gu8_bytes = touched * 2.0 * wl.I * wl.d + wl.T * wl.d * 2.0  # FP8 codes: one byte per weight
     result["prefill_fp8"] = {"ms_per_step": total8 / args.steps, "tokens_per_s": wl.T * args.steps / (total8 * 1e-3),
                              "stages_ms": st8,
                              "gate_up_GBps": gu8_bytes / (st8["gate_up"] * 1e-3) / 1e9,
@@ -467,6 +522,23 @@ def main():
         log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
     del st
     torch.cuda.empty_cache()
+    if not args.no_extra:
+        for name in ("small", "skewed"):
+            if name == wl.name:
+                continue
+            xw = configs.get(name)
+            xst = setup(xw, dev)
+            xtotal, xstages = run_steps(lm, xst, args.steps, args.warmup)
+            xm = layer_measures(xw, xst, xtotal, xstages, args.steps)
+            xm["config"] = {"workload": xw.description, "T": xw.T, "d": xw.d, "N": xw.N, "Z": xw.Z,
+                            "K": xw.K, "I": xw.I}
+            result[name] = xm
+            xr = xm["roofline"]
+            log(f"{name}: {xm['ms_per_step']:.3f} ms/step; gate_up {xr['mfma_tflops']:.0f} TFLOP/s "
+                f"({xr['mfma_frac']:.1%}), {xr['hbm_GBps']:.0f} GB/s; FFN {xm['ffn']['TFLOPs']:.0f} TFLOP/s "
+                f"({xm['ffn']['mfma_frac']:.1%}); bound {xr['bound']} at {xr['frac']:.1%}")
+            del xst
+            torch.cuda.empty_cache()
     if not args.no_decode:
         result["decode"] = decode_runs(lm, dev, max(5, args.steps), args.warmup)
     print(json.dumps(result), flush=True)
