@@ -164,7 +164,9 @@ lc_moe_status lc_moe_forward(const lc_moe_shape* shape, const void* x,
 
 /* lc_moe_forward with instrumentation: when stage_events is not NULL it holds
  * LC_MOE_NUM_STAGES + 1 events created by the caller; event 0 is recorded on the stream
- * before the first stage and event i+1 after stage i.  Same results as lc_moe_forward. */
+ * before the first stage and event i+1 after stage i.  Same results as lc_moe_forward.
+ * A layer of at most 256 tokens runs the top-K and the permutation as one kernel; it is
+ * counted in the route stage and the permute stage's span is empty. */
 lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
                                     const lc_moe_weights* weights, void* y, int32_t* topk_idx,
                                     float* topk_gate, int32_t* load, void* workspace,

@@ -227,13 +227,22 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   void* hbuf = at<char>(workspace, p.hbuf);
   void* ybuf = at<char>(workspace, p.ybuf);
 
+  // A layer of one token block runs top-K and permutation as one kernel (counted in the
+  // route stage; the permute stage's span is then empty).
+  const bool fused = p.nblocks == 1;
+  int32_t* done = at<int32_t>(workspace, p.done);
   if (!mark(0)) return LC_MOE_E_DEVICE;
   LCM_LAUNCH(launch_router_logits(s, x, weights->w_router, at<bf16_t>(workspace, p.wsplit),
                                   at<float>(workspace, p.logits), at<float>(workspace, p.rpart),
-                                  stream));
-  LCM_LAUNCH(launch_router_topk(s, at<float>(workspace, p.logits), weights->bias, idx, gate, stream));
+                                  stream, fused ? done : nullptr));
+  if (fused)
+    LCM_LAUNCH(launch_topk_permute(s, at<float>(workspace, p.logits), weights->bias, idx, gate, done, ld,
+                                   offsets, at<MTile>(workspace, p.mtiles), at<int32_t>(workspace, p.n_mtiles),
+                                   p.bm, slot_row, perm_token, stream));
+  else
+    LCM_LAUNCH(launch_router_topk(s, at<float>(workspace, p.logits), weights->bias, idx, gate, stream));
   if (!mark(1)) return LC_MOE_E_DEVICE;
-  LCM_CHECK(permute_core(s, idx, p, workspace, ld, offsets, slot_row, perm_token, nullptr, stream));
+  if (!fused) LCM_CHECK(permute_core(s, idx, p, workspace, ld, offsets, slot_row, perm_token, nullptr, stream));
   if (!mark(2)) return LC_MOE_E_DEVICE;
   LCM_LAUNCH(launch_ffn_gate_up(s, x, perm_token, weights->w_gate, weights->w_up, weights->fp8,
                                 weights->packed, hbuf, mtiles, offsets, n_mtiles, p.mt_max, stream));

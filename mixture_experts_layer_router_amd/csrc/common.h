@@ -105,7 +105,7 @@ inline bool router_fused_split(const lc_moe_shape& s) {
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsPlan {
   size_t logits, wsplit, rpart, idx, gate, block_counts, block_base, load, offsets, mtiles,
-      n_mtiles, perm_token, slot_row, hbuf, ybuf, total;
+      n_mtiles, done, perm_token, slot_row, hbuf, ybuf, total;
   int nblocks;  // token blocks of the permutation
   int bm;       // M-tile height for this dtype
   int mt_max;   // capacity of the M-tile list
@@ -139,6 +139,7 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   p.offsets = take((N + 1) * 4);
   p.mtiles = take(mt * sizeof(MTile));
   p.n_mtiles = take(4);
+  p.done = take(4);  // workgroups done with their top-K (fused top-K + permutation)
   p.perm_token = take(tk * 4);
   p.slot_row = take(tk * 4);
   p.hbuf = take(tk * size_t(s.I) * es);
@@ -246,8 +247,11 @@ inline PackPlan plan_packed(const lc_moe_shape& s) {
 // three bf16 parts (wsplit, 3*E*d bf16); with more than one split (router_split) the
 // GEMM writes `splits` partial logit arrays [splits][T][E] to rpart, which are then summed
 // in split order into logits.
+// When zero_word is not NULL, the kernel also sets *zero_word = 0 (the counter of the fused
+// top-K + permutation kernel that follows it on the stream).
 hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
-                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st);
+                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st,
+                                int32_t* zero_word = nullptr);
 // Softmax over E, biased top-K; writes idx [T][K] and gate [T][K].
 hipError_t launch_router_topk(const lc_moe_shape& s, const float* logits, const float* bias,
                               int32_t* idx, float* gate, hipStream_t st);
@@ -264,6 +268,14 @@ hipError_t launch_permute_small(const lc_moe_shape& s, const int32_t* idx, int32
                                 int32_t* ffn_cnt, int32_t* offsets, MTile* mtiles,
                                 int32_t* n_mtiles, int bm, int32_t* slot_row, int32_t* perm_token,
                                 hipStream_t st);
+// The forward of a layer of one token block: softmax + biased top-K (idx, gate), then, in
+// the workgroup that finishes last, the permutation (load, offsets, M-tile list, slot_row,
+// perm_token) -- one launch for router_topk + permute_small.  *done must be 0 on entry
+// (launch_router_logits zeroes it).
+hipError_t launch_topk_permute(const lc_moe_shape& s, const float* logits, const float* bias,
+                               int32_t* idx, float* gate, int32_t* done, int32_t* load,
+                               int32_t* offsets, MTile* mtiles, int32_t* n_mtiles, int bm,
+                               int32_t* slot_row, int32_t* perm_token, hipStream_t st);
 // Stable scatter: slot_row [T][K], perm_token [nnz].
 hipError_t launch_scatter(const lc_moe_shape& s, const int32_t* idx, const int32_t* block_base,
                           int nblocks, int32_t* slot_row, int32_t* perm_token, hipStream_t st);

@@ -14,6 +14,7 @@
 // the mask's atomicOr then returns the bit already set, and the block ranks its picks one
 // by one in (token, pick) order instead, so every pick still gets its own row.
 #include "common.h"
+#include "topk.h"
 
 namespace lcm {
 
@@ -181,25 +182,31 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // Layers of one token block (T <= 256, decode): histogram, scan and scatter in one
-// workgroup of 1024 threads, with the counts, the wave masks and the offsets in LDS; the
-// three kernels above are each a few microseconds of mostly launch and latency at this
-// size.  The same integer rules, so the same results: token t is thread t (wave t / 64,
-// lane t % 64), its rank for expert e is popcount(mask of e in its wave, lanes below) plus
-// the picks of e by earlier waves, and its row is offsets[e] + rank.
-__global__ __launch_bounds__(1024) void permute_small_kernel(
-    const int32_t* __restrict__ idx, int T, int K, int E, int N, int bm,
-    int32_t* __restrict__ load, int32_t* __restrict__ ffn_cnt, int32_t* __restrict__ offsets,
-    MTile* __restrict__ mtiles, int32_t* __restrict__ n_mtiles, int32_t* __restrict__ slot_row,
-    int32_t* __restrict__ perm_token) {
-  __shared__ int cnt[kMaxE];
-  __shared__ unsigned long long masks[4 * kMaxN];  // [wave][expert]
-  __shared__ int off[kMaxN];
-  __shared__ int part[1024], part2[1024];
-  __shared__ int repeated;  // a token picks an expert twice: rank one by one (as scatter_kernel)
+// workgroup, with the counts, the wave masks and the offsets in LDS; the three kernels
+// above are each a few microseconds of mostly launch and latency at this size.  The same
+// integer rules, so the same results: token t is thread t (wave t / 64, lane t % 64), its
+// rank for expert e is popcount(mask of e in its wave, lanes below) plus the picks of e by
+// earlier waves, and its row is offsets[e] + rank.  NT threads (NT >= 256: waves 0..3 hold
+// the tokens).
+struct BlockLds {
+  int cnt[kMaxE];
+  unsigned long long masks[4 * kMaxN];  // [wave][expert]
+  int off[kMaxN];
+  int part[1024], part2[1024];
+  int repeated;  // a token picks an expert twice: rank one by one (as scatter_kernel)
+  int last;      // fused kernel: this workgroup finished last
+};
+
+template <int NT>
+__device__ void permute_block(BlockLds& L, const int32_t* __restrict__ idx, int T, int K, int E,
+                              int N, int bm, int32_t* __restrict__ load, int32_t* __restrict__ ffn_cnt,
+                              int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+                              int32_t* __restrict__ n_mtiles, int32_t* __restrict__ slot_row,
+                              int32_t* __restrict__ perm_token) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-  for (int i = tid; i < 4 * N; i += 1024) masks[i] = 0ull;
-  if (tid == 0) repeated = 0;
+  for (int e = tid; e < E; e += NT) L.cnt[e] = 0;
+  for (int i = tid; i < 4 * N; i += NT) L.masks[i] = 0ull;
+  if (tid == 0) L.repeated = 0;
   __syncthreads();
   const int t = tid;  // T <= 256: tokens on waves 0..3
   if (t < T) {
@@ -207,47 +214,47 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     for (int k = 0; k < K; ++k) {
       const int e = idx[size_t(t) * K + k];
       if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
-        atomicAdd(&cnt[e], 1);  // integer: exact whatever the order
+        atomicAdd(&L.cnt[e], 1);  // integer: exact whatever the order
         if (e < N) {
           ++f;
           const unsigned long long bit = 1ull << lane;
-          if (atomicOr(&masks[w * N + e], bit) & bit) repeated = 1;
+          if (atomicOr(&L.masks[w * N + e], bit) & bit) L.repeated = 1;
         }
       }
     }
     if (ffn_cnt) ffn_cnt[t] = f;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) load[e] = cnt[e];
+  for (int e = tid; e < E; e += NT) load[e] = L.cnt[e];
   // exclusive scans over the N FFN experts of rows and of M-tiles (as in scan_kernel)
-  const int per = (N + 1023) / 1024;
+  const int per = (N + NT - 1) / NT;
   int rs = 0, ms = 0;
   for (int i = 0; i < per; ++i) {
     const int e = tid * per + i;
     if (e < N) {
-      rs += cnt[e];
-      ms += (cnt[e] + bm - 1) / bm;
+      rs += L.cnt[e];
+      ms += (L.cnt[e] + bm - 1) / bm;
     }
   }
-  part[tid] = rs;
-  part2[tid] = ms;
+  L.part[tid] = rs;
+  L.part2[tid] = ms;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-    const int a = tid >= o ? part[tid - o] : 0;
-    const int c = tid >= o ? part2[tid - o] : 0;
+  for (int o = 1; o < NT; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= o ? L.part[tid - o] : 0;
+    const int c = tid >= o ? L.part2[tid - o] : 0;
     __syncthreads();
-    part[tid] += a;
-    part2[tid] += c;
+    L.part[tid] += a;
+    L.part2[tid] += c;
     __syncthreads();
   }
-  int r = tid > 0 ? part[tid - 1] : 0;
-  int m = tid > 0 ? part2[tid - 1] : 0;
+  int r = tid > 0 ? L.part[tid - 1] : 0;
+  int m = tid > 0 ? L.part2[tid - 1] : 0;
   for (int i = 0; i < per; ++i) {
     const int e = tid * per + i;
     if (e < N) {
-      off[e] = r;
+      L.off[e] = r;
       offsets[e] = r;
-      const int rows = cnt[e];
+      const int rows = L.cnt[e];
       const int nt = (rows + bm - 1) / bm;
       for (int j = 0; j < nt; ++j) {
         MTile mt;
@@ -261,13 +268,13 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
       m += nt;
     }
   }
-  if (tid == 1023) {
-    offsets[N] = part[1023];
-    *n_mtiles = part2[1023];
+  if (tid == NT - 1) {
+    offsets[N] = L.part[NT - 1];
+    *n_mtiles = L.part2[NT - 1];
   }
   __syncthreads();
-  if (repeated) {  // uniform over the workgroup
-    if (tid == 0) scatter_serial(idx, 0, T, K, N, off, slot_row, perm_token);
+  if (L.repeated) {  // uniform over the workgroup
+    if (tid == 0) scatter_serial(idx, 0, T, K, N, L.off, slot_row, perm_token);
     return;
   }
   if (t < T) {
@@ -276,14 +283,52 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
       const int e = idx[size_t(t) * K + k];
       int row = -1;
       if (static_cast<unsigned>(e) < static_cast<unsigned>(N)) {
-        int rank = __popcll(masks[w * N + e] & below_lane);
-        for (int ww = 0; ww < w; ++ww) rank += __popcll(masks[ww * N + e]);
-        row = off[e] + rank;
+        int rank = __popcll(L.masks[w * N + e] & below_lane);
+        for (int ww = 0; ww < w; ++ww) rank += __popcll(L.masks[ww * N + e]);
+        row = L.off[e] + rank;
         perm_token[row] = t;
       }
       slot_row[size_t(t) * K + k] = row;
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int E, int N, int bm,
+    int32_t* __restrict__ load, int32_t* __restrict__ ffn_cnt, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ n_mtiles, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ perm_token) {
+  __shared__ BlockLds L;
+  permute_block<1024>(L, idx, T, K, E, N, bm, load, ffn_cnt, offsets, mtiles, n_mtiles, slot_row,
+                      perm_token);
+}
+
+// Top-K and the one-block permutation in one kernel, for the forward of layers of one token
+// block (T <= 256): the top-K runs as in router_topk_kernel, one wavefront per token and
+// four tokens per workgroup; then each workgroup counts itself done on a device-scope
+// counter, and the workgroup that finishes last runs the permutation above on every
+// token's picks.  The counter is zeroed by the router-logits kernel that runs just before
+// on the same stream, so no memset is needed (the kernel can be captured into a graph).
+// Same picks, gates and permutation as the separate kernels, bit for bit.
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_permute_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int K, int E, int N,
+    int bm, int32_t* __restrict__ idx, float* __restrict__ gate, int32_t* __restrict__ done,
+    int32_t* __restrict__ load, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+    int32_t* __restrict__ n_mtiles, int32_t* __restrict__ slot_row, int32_t* __restrict__ perm_token) {
+  __shared__ BlockLds L;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < T)
+    router_topk_token<EPL>(logits + size_t(t) * E, bias, E, K, threadIdx.x & 63, idx + size_t(t) * K,
+                           gate + size_t(t) * K);
+  __threadfence();  // this workgroup's picks are visible device-wide before it counts itself
+  __syncthreads();
+  if (threadIdx.x == 0) L.last = atomicAdd(done, 1) == int(gridDim.x) - 1;
+  __syncthreads();
+  if (!L.last) return;
+  __threadfence();  // the other workgroups' picks, published before their increments
+  permute_block<256>(L, idx, T, K, E, N, bm, load, nullptr, offsets, mtiles, n_mtiles, slot_row,
+                     perm_token);
 }
 
 // One workgroup per row; rows from offsets[N] on exit at once.
@@ -330,6 +375,26 @@ hipError_t launch_permute_small(const lc_moe_shape& s, const int32_t* idx, int32
                                 hipStream_t st) {
   hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, s.T, s.K, s.N + s.Z, s.N,
                      bm, load, ffn_cnt, offsets, mtiles, n_mtiles, slot_row, perm_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_permute(const lc_moe_shape& s, const float* logits, const float* bias,
+                               int32_t* idx, float* gate, int32_t* done, int32_t* load,
+                               int32_t* offsets, MTile* mtiles, int32_t* n_mtiles, int bm,
+                               int32_t* slot_row, int32_t* perm_token, hipStream_t st) {
+  const int E = s.N + s.Z;
+  const int epl = (E + 63) / 64;
+  const dim3 grid((s.T + 3) / 4), block(256);
+#define LCM_TOPK(n)                                                                        \
+  hipLaunchKernelGGL(topk_permute_kernel<n>, grid, block, 0, st, logits, bias, s.T, s.K, E, s.N, \
+                     bm, idx, gate, done, load, offsets, mtiles, n_mtiles, slot_row, perm_token)
+  if (epl <= 2) LCM_TOPK(2);
+  else if (epl <= 4) LCM_TOPK(4);
+  else if (epl <= 8) LCM_TOPK(8);
+  else if (epl <= 16) LCM_TOPK(16);
+  else if (epl <= 32) LCM_TOPK(32);
+  else LCM_TOPK(64);
+#undef LCM_TOPK
   return hipGetLastError();
 }
 

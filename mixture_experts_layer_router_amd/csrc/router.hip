@@ -16,12 +16,7 @@
 
 #include "common.h"
 #include "lds_dma.h"
-
-// Wavefront reductions of the ROCm device library (ockl): DPP steps in a fixed order, the
-// result in every active lane.
-extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
-extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
-extern "C" __device__ __attribute__((const)) int __ockl_wfred_min_i32(int);
+#include "topk.h"
 
 namespace lcm {
 
@@ -62,8 +57,10 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 
 __global__ __launch_bounds__(256, 2) void router_logits_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, float* __restrict__ out,
-    int T, int d, int E, int chunk) {
+    int T, int d, int E, int chunk, int32_t* __restrict__ zero_word) {
   using namespace rl;
+  if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *zero_word = 0;
+
   __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDA];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[3][BN * LDA];
 
@@ -201,9 +198,11 @@ constexpr int LPW = (NL + 7) / 8;          // load slots per wave (7)
 template <bool FSPLIT>
 __global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wsplit, const float* __restrict__ wr,
-    float* __restrict__ out, int T, int d, int E, int chunk, int n_et, int splits, int n_units) {
+    float* __restrict__ out, int T, int d, int E, int chunk, int n_et, int splits, int n_units,
+    int32_t* __restrict__ zero_word) {
   using namespace rp;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+  if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *zero_word = 0;
 
   const int per = (n_units + 7) >> 3;
   const int wslot = blockIdx.x >> 3;
@@ -398,7 +397,8 @@ __global__ __launch_bounds__(512, 1) void router_logits_pipe_kernel(
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, float* __restrict__ logits,
-    int T, int d, int E) {
+    int T, int d, int E, int32_t* __restrict__ zero_word) {
+  if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *zero_word = 0;
   __shared__ float Xs[64][17];
   __shared__ float Ws[64][17];
   const int tid = threadIdx.x;
@@ -431,8 +431,7 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Softmax + biased top-K: one wavefront per token, EPL experts per lane
-// (expert e lives in lane e % 64, slot e / 64).
+// Softmax + biased top-K: one wavefront per token (router_topk_token in topk.h).
 // ---------------------------------------------------------------------------------------
 template <int EPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
@@ -440,79 +439,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int32_t* __restrict__ idx,
                                                           float* __restrict__ gate, int T,
                                                           int E, int K) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + size_t(t) * E;
-  // All loads first, unconditionally (slots past E read expert E-1 and are masked below),
-  // so they are in flight together: loads under per-slot branches each waited on their own,
-  // and a token's chain then took one memory latency per slot.
-  float v[EPL], b[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    const int ec = e < E ? e : E - 1;
-    v[j] = row[ec];
-    b[j] = bias[ec];
-  }
-  // keeps the bias loads here: left alone, the compiler sinks them to their use after the
-  // softmax, a second memory round trip on each token's chain
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) asm volatile("" : "+v"(v[j]), "+v"(b[j]));
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? v[j] : -INFINITY;
-    m = fmaxf(m, v[j]);
-  }
-  // wavefront reductions (DPP, fixed order; every lane gets the same result)
-  m = __ockl_wfred_max_f32(m);
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? expf(v[j] - m) : 0.f;
-    sum += v[j];
-  }
-  sum = __ockl_wfred_add_f32(sum);
-  float s[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = v[j] / sum;  // p, IEEE division
-    s[j] = e < E ? v[j] + b[j] : -INFINITY;
-  }
-  // K rounds: the largest s left wins, the lowest expert index among equal s.  Each round
-  // takes the lane's best remaining slot (ascending slots keep the lower index), the
-  // wavefront maximum of those, then the lowest expert index holding that maximum.
-  // Branch-free: slots past E and taken slots hold -inf, so "the first remaining slot, then
-  // any strictly larger one" is s > bv from bv = -inf (equal s keep the lower slot).
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const bool better = s[j] > bv;
-      bv = better ? s[j] : bv;
-      be = better ? lane + 64 * j : be;
-    }
-    const float wm = __ockl_wfred_max_f32(bv);
-    const int we = __ockl_wfred_min_i32(bv == wm ? be : 0x7fffffff);
-    const bool mine = (we & 63) == lane;
-    const int jw = we >> 6;
-    float p = 0.f;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const bool hit = mine && j == jw;
-      p = hit ? v[j] : p;
-      s[j] = hit ? -INFINITY : s[j];  // taken
-    }
-    if (mine) {
-      idx[size_t(t) * K + k] = we;
-      gate[size_t(t) * K + k] = p;
-    }
-  }
+  router_topk_token<EPL>(logits + size_t(t) * E, bias, E, K, threadIdx.x & 63, idx + size_t(t) * K,
+                         gate + size_t(t) * K);
 }
 
 // logits = sum of the split partials, added in split order (n = T*E, 4 per thread).  The
@@ -550,7 +480,8 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 }
 
 hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const float* w_router,
-                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st) {
+                                bf16_t* wsplit, float* logits, float* rpart, hipStream_t st,
+                                int32_t* zero_word) {
   const int E = s.N + s.Z;
   if (s.dtype == LC_MOE_BF16) {
     const size_t n = size_t(E) * s.d;  // a multiple of 8
@@ -569,15 +500,15 @@ hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const floa
       if (fsplit)
         hipLaunchKernelGGL(router_logits_pipe_kernel<true>, grid, dim3(512), 0, st,
                            static_cast<const bf16_t*>(x), wsplit, w_router, dst, s.T, s.d, E, rs.chunk,
-                           n_et, rs.splits, units);
+                           n_et, rs.splits, units, zero_word);
       else
         hipLaunchKernelGGL(router_logits_pipe_kernel<false>, grid, dim3(512), 0, st,
                            static_cast<const bf16_t*>(x), wsplit, w_router, dst, s.T, s.d, E, rs.chunk,
-                           n_et, rs.splits, units);
+                           n_et, rs.splits, units, zero_word);
     } else {
       dim3 grid((E + rl::BN - 1) / rl::BN, (s.T + rl::BM - 1) / rl::BM, rs.splits);
       hipLaunchKernelGGL(router_logits_bf16_kernel, grid, dim3(256), 0, st,
-                         static_cast<const bf16_t*>(x), wsplit, dst, s.T, s.d, E, rs.chunk);
+                         static_cast<const bf16_t*>(x), wsplit, dst, s.T, s.d, E, rs.chunk, zero_word);
     }
     if (rs.splits > 1) {
       const size_t nl = size_t(s.T) * E;
@@ -587,7 +518,7 @@ hipError_t launch_router_logits(const lc_moe_shape& s, const void* x, const floa
   } else {
     dim3 grid((E + 63) / 64, (s.T + 63) / 64);
     hipLaunchKernelGGL(router_logits_f32_kernel, grid, dim3(256), 0, st,
-                       static_cast<const float*>(x), w_router, logits, s.T, s.d, E);
+                       static_cast<const float*>(x), w_router, logits, s.T, s.d, E, zero_word);
   }
   return hipGetLastError();
 }
