@@ -12,6 +12,8 @@ Modules:
   bruteforce  scalar pure-Python formulation for tiny inputs (pins moe)
   dense       dense-masked formulation of the combine (pins moe's permute/combine)
   controller  expert-bias PID controller (one update of the selection bias from loads)
+  backward    gradients of the grouped SwiGLU FFN (dx and every expert's dW) for fixed
+              picks and gates
   fp8         block-FP8 expert weights: E4M3 encode/decode, power-of-two block scales,
               quantize / dequantize
   tune_routing_inputs
