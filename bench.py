@@ -1,7 +1,7 @@
 """Benchmark of the zero-computation-expert MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--no-decode] [--no-extra] [--no-cpu-baseline] [--no-packed]
+                    [--no-decode] [--no-extra] [--no-backward] [--no-cpu-baseline] [--no-packed]
                     [--no-overlap] [--calib-copy]
 
 One step = one lc_moe_forward (router, permutation, grouped SwiGLU FFN, combine) over the
@@ -33,6 +33,8 @@ this size the same bits as the row-major weights).
 prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
 overlap: a dense SwiGLU FFN (width 2d) over the same tokens beside the layer, serial on one
 stream against concurrent on two streams.
+backward: lc_moe_ffn_backward (dx and every expert's dW) for the forward's picks and a
+seeded dy, timed over its 8 grouped GEMMs' FLOPs.
 cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -315,6 +317,45 @@ def graph_ms(lm, st, steps):
     return ms
 
 
+def backward_run(lm, st, wl, steps, warmup):
+    """lc_moe_ffn_backward for the layer's own picks and gates (from the timed forward) and a
+    seeded dy; returns ms per call and the rate of its 8 grouped GEMMs (16*d*I FLOPs per FFN
+    pick: G and U recomputed, dH, dX (two), dW_down, dW_gate, dW_up)."""
+    import torch
+    from inputs.generate import upstream_grad
+    dev = st["x"].device
+    o = st["outs"]
+    dy = torch.from_numpy(upstream_grad(wl).view(np.int16)).view(torch.bfloat16).to(dev)
+    w = st["w"]
+    shape = lm.make_shape(wl.T, wl.d, wl.N, wl.Z, wl.K, wl.I, lm.BF16)
+    ws = torch.empty(lm.lc_moe_backward_workspace_size(shape), dtype=torch.uint8, device=dev)
+    out = dict(dx=torch.empty_like(st["x"]), dw_gate=torch.empty_like(w["gate"]), dw_up=torch.empty_like(w["up"]),
+               dw_down=torch.empty_like(w["down"]))
+    wts = lm._weights(None, None, w["gate"], w["up"], w["down"])
+
+    def call():
+        lm.lc_moe_ffn_backward(shape, st["x"], wts, o["idx"], o["gate"], dy, out["dx"], out["dw_gate"],
+                               out["dw_up"], out["dw_down"], ws)
+
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nnz = int(o["load"][:wl.N].sum())
+    flops = 16.0 * wl.d * wl.I * nnz
+    res = {"ms": ms, "flops": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+           "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    del out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def dense_ffn_setup(lm, wl, dev, i_dense):
     """A dense SwiGLU FFN over all T tokens (width i_dense), expressed as the layer with one
     FFN expert, no zero experts and K = 1: the router over one expert gives gate 1 exactly,
@@ -439,6 +480,7 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the dense-FFN-beside-the-layer two-stream measurement")
     ap.add_argument("--no-extra", action="store_true", help="skip the small and skewed layers")
+    ap.add_argument("--no-backward", action="store_true", help="skip the FFN backward timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 4 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -511,6 +553,12 @@ def main():
     log(f"FP8 weights: {total8 / args.steps:.3f} ms/step; stages "
         f"{json.dumps({k: round(v, 4) for k, v in st8.items()})}")
     st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"])
+    if not args.no_backward and wl.dtype == "bf16":
+        run_steps(lm, st, 1, 0)  # the row-major forward's picks and gates
+        result["backward"] = backward_run(lm, st, wl, max(3, args.steps // 4), 1)
+        bw = result["backward"]
+        log(f"backward (dx, dW_gate, dW_up, dW_down): {bw['ms']:.3f} ms, {bw['TFLOPs']:.0f} TFLOP/s "
+            f"({bw['mfma_frac']:.1%} of the bf16 peak)")
     if not args.no_overlap:
         result["overlap"] = overlap_run(lm, st, wl, max(3, args.steps // 2), 2 * wl.d)
         ov = result["overlap"]

@@ -236,6 +236,38 @@ lc_moe_status lc_moe_pack_weights(const lc_moe_shape* shape, const void* w_gate,
                                   const void* w_up, const void* w_down, void* packed_weights,
                                   size_t packed_weights_bytes, hipStream_t stream);
 
+/* Backward of the grouped SwiGLU FFN, for training.  The pages describe the model's
+ * training (LongCat-Flash article, section "Model scaling and multi-stage training") but no
+ * backward pass; this is the plain gradient of the layer's sum (section "Zero-computation
+ * experts") with the routing held fixed: given the forward's picks topk_idx and gates
+ * topk_gate and the gradient dy of the layer output y, it computes the gradients of
+ * L = sum_t <dy_t, y_t> with respect to x and the three matrices of every FFN expert.  For
+ * an FFN pick (t, i) with gate g, with G = W_gate x_t, U = W_up x_t, s = sigmoid(G),
+ * a = G s, H = a U:
+ *   dH = g W_down^T dy_t;  dG = dH U (s + a (1 - s));  dU = dH a
+ *   dW_down += g dy_t H^T;  dW_gate += dG x_t^T;  dW_up += dU x_t^T
+ *   dx_t += W_gate^T dG + W_up^T dU
+ * and a zero-computation pick adds g dy_t to dx_t.  The router's gradient (through the
+ * gates and the softmax) is not part of it.  bf16 layers with d and I multiples of 32
+ * (else LC_MOE_E_DTYPE / LC_MOE_E_SHAPE); row-major weights (weights->w_gate, w_up,
+ * w_down; the router, bias, fp8 and packed fields are not read).  Arithmetic: bf16
+ * operands, fp32 accumulation; the row intermediates g*H, dG, dU and dX are rounded to
+ * bf16, dH is kept in fp32; each token's dx adds its FFN picks' rows in pick order, then
+ * its zero picks' gate sum times dy_t, in fp32, and is rounded once.  Deterministic.
+ *   x          [T][d] bf16            the forward's input
+ *   topk_idx   [T][K] int32, topk_gate [T][K] fp32   the forward's picks and gates
+ *   dy         [T][d] bf16            gradient of y
+ *   dx         [T][d] bf16 (out)
+ *   dw_gate, dw_up [N][I][d], dw_down [N][d][I] bf16 (out); an expert without rows gets zeros
+ * The workspace (lc_moe_backward_workspace_size; 0 for shapes without a backward) holds the
+ * permutation of the picks and the row intermediates (about (T*K) * (12*I + 2*d) bytes). */
+size_t lc_moe_backward_workspace_size(const lc_moe_shape* shape);
+lc_moe_status lc_moe_ffn_backward(const lc_moe_shape* shape, const void* x,
+                                  const lc_moe_weights* weights, const int32_t* topk_idx,
+                                  const float* topk_gate, const void* dy, void* dx, void* dw_gate,
+                                  void* dw_up, void* dw_down, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* PID gains of the expert-bias controller (host struct). */
 typedef struct {
   float kp, ki, kd;

@@ -30,7 +30,7 @@ import numpy as np
 
 from .configs import Workload
 
-TAG_X, TAG_WR, TAG_B, TAG_WG, TAG_WU, TAG_WD, TAG_PERM, TAG_XR = range(8)
+TAG_X, TAG_WR, TAG_B, TAG_WG, TAG_WU, TAG_WD, TAG_PERM, TAG_XR, TAG_DY = range(9)
 
 TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "routing_tables.json")
 
@@ -178,6 +178,13 @@ def expert_weights(wl: Workload, device="cpu") -> dict:
             w[e].copy_((r * wl.expert_std).to(tdt))
         out[name] = w
     return out
+
+
+def upstream_grad(wl: Workload) -> np.ndarray:
+    """A seeded gradient dy [T,d] of the layer output for the backward: standard normal,
+    stored like x (bf16 bits for bf16 workloads, float32 otherwise)."""
+    g = rng(*wl.seed_key, TAG_DY, 0).standard_normal((wl.T, wl.d))
+    return f64_to_bf16_bits(g) if wl.dtype == "bf16" else g.astype(np.float32)
 
 
 def weights_f64(t) -> np.ndarray:

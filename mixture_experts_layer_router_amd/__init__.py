@@ -8,7 +8,7 @@ device memory and streams.  The library is opened on first use and a missing bui
 
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
 ``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_forward_noalloc``,
-``lc_moe_bias_update``,
+``lc_moe_ffn_backward``, ``lc_moe_backward_workspace_size``, ``lc_moe_bias_update``,
 ``lc_moe_quantize_weights``, ``lc_moe_fp8_weights_size``, ``lc_moe_pack_weights``,
 ``lc_moe_packed_weights_size``, ``lc_moe_workspace_size``); ``route``, ``expert_load``,
 ``permute``, ``forward``, ``bias_update``, ``quantize_weights`` and ``pack_weights``
@@ -62,6 +62,9 @@ _SIG = {
                                              _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "lc_moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights), _vp,
                                               _vp, _vp, _vp, _vp]),
+    "lc_moe_backward_workspace_size": (_sz, [ctypes.POINTER(Shape)]),
+    "lc_moe_ffn_backward": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, ctypes.POINTER(Weights), _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_fp8_weights_size": (_sz, [ctypes.POINTER(Shape)]),
     "lc_moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_packed_weights_size": (_sz, [ctypes.POINTER(Shape)]),
@@ -217,6 +220,18 @@ def lc_moe_forward_staged(shape, x, weights: Weights, y, topk_idx, topk_gate, lo
            "lc_moe_forward_staged")
 
 
+def lc_moe_backward_workspace_size(shape: Shape) -> int:
+    return int(lib().lc_moe_backward_workspace_size(ctypes.byref(shape)))
+
+
+def lc_moe_ffn_backward(shape, x, weights: Weights, topk_idx, topk_gate, dy, dx, dw_gate, dw_up, dw_down,
+                        workspace, stream=None):
+    _check(lib().lc_moe_ffn_backward(ctypes.byref(shape), _ptr(x), ctypes.byref(weights), _ptr(topk_idx),
+                                    _ptr(topk_gate), _ptr(dy), _ptr(dx), _ptr(dw_gate), _ptr(dw_up),
+                                    _ptr(dw_down), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "lc_moe_ffn_backward")
+
+
 def lc_moe_bias_update(shape, gains: Pid, load, target, bias, integral, prev_err, stream=None):
     _check(lib().lc_moe_bias_update(ctypes.byref(shape), ctypes.byref(gains), _ptr(load),
                                    _ptr(target), _ptr(bias), _ptr(integral), _ptr(prev_err),
@@ -300,6 +315,27 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_ev
     else:
         lc_moe_forward_staged(shape, x, wts, y, idx, gate, load, ws, stage_events=stage_events)
     return dict(y=y, topk_idx=idx, topk_gate=gate, load=load)
+
+
+def ffn_backward(x, w_gate, w_up, w_down, topk_idx, topk_gate, dy, Z, workspace=None):
+    """dict(dx, dw_gate, dw_up, dw_down): gradients of sum <dy, y> for the forward's picks
+    and gates (held fixed); x, dy [T,d] bf16; w_gate/w_up [N,I,d]; w_down [N,d,I]; Z = number
+    of zero-computation experts of the layer."""
+    import torch
+    N, I, d = w_gate.shape
+    T, K = topk_idx.shape
+    shape = make_shape(T, d, N, Z, K, I, x.dtype)
+    if workspace is None:
+        n = lc_moe_backward_workspace_size(shape)
+        if n == 0:
+            raise LcMoeError(2, "lc_moe_backward_workspace_size")
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    out = dict(dx=torch.empty_like(x), dw_gate=torch.empty_like(w_gate), dw_up=torch.empty_like(w_up),
+               dw_down=torch.empty_like(w_down))
+    wts = _weights(None, None, w_gate, w_up, w_down)
+    lc_moe_ffn_backward(shape, x, wts, topk_idx, topk_gate, dy, out["dx"], out["dw_gate"], out["dw_up"],
+                        out["dw_down"], workspace)
+    return out
 
 
 def bias_update(load, target, bias, integral, prev_err, T, K, N, kp, ki, kd):

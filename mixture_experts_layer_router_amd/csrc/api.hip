@@ -324,6 +324,57 @@ lc_moe_status lc_moe_forward_noalloc(const lc_moe_shape* shape, const void* x,
                                LC_MOE_STATIC_WORKSPACE_BYTES, stream, nullptr);
 }
 
+size_t lc_moe_backward_workspace_size(const lc_moe_shape* shape) {
+  if (check_shape(shape) != LC_MOE_OK || shape->dtype != LC_MOE_BF16 || shape->d % 32 || shape->I % 32) return 0;
+  return plan_backward(*shape).total;
+}
+
+lc_moe_status lc_moe_ffn_backward(const lc_moe_shape* shape, const void* x,
+                                  const lc_moe_weights* weights, const int32_t* topk_idx,
+                                  const float* topk_gate, const void* dy, void* dx, void* dw_gate,
+                                  void* dw_up, void* dw_down, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  LCM_CHECK(check_shape(shape));
+  if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
+  if (shape->d % 32 || shape->I % 32) return LC_MOE_E_SHAPE;
+  if (!weights) return LC_MOE_E_NULLPTR;
+  LCM_CHECK(check_ptr(x));
+  LCM_CHECK(check_ptr(weights->w_gate));
+  LCM_CHECK(check_ptr(weights->w_up));
+  LCM_CHECK(check_ptr(weights->w_down));
+  LCM_CHECK(check_ptr(topk_idx));
+  LCM_CHECK(check_ptr(topk_gate));
+  LCM_CHECK(check_ptr(dy));
+  LCM_CHECK(check_ptr(dx));
+  LCM_CHECK(check_ptr(dw_gate));
+  LCM_CHECK(check_ptr(dw_up));
+  LCM_CHECK(check_ptr(dw_down));
+  if (!workspace) return LC_MOE_E_NULLPTR;
+  if (!aligned16(workspace)) return LC_MOE_E_ALIGN;
+  const BwPlan p = plan_backward(*shape);
+  if (workspace_bytes < p.total) return LC_MOE_E_WORKSPACE;
+  const lc_moe_shape& s = *shape;
+  int32_t* load = at<int32_t>(workspace, p.load);
+  int32_t* offsets = at<int32_t>(workspace, p.offsets);
+  int32_t* slot_row = at<int32_t>(workspace, p.slot_row);
+  int32_t* perm_token = at<int32_t>(workspace, p.perm_token);
+  MTile* mtiles = at<MTile>(workspace, p.mtiles);
+  int32_t* n_mtiles = at<int32_t>(workspace, p.n_mtiles);
+  if (p.nblocks == 1) {
+    LCM_LAUNCH(launch_permute_small(s, topk_idx, load, nullptr, offsets, mtiles, n_mtiles, kBmBwd, slot_row,
+                                    perm_token, stream));
+  } else {
+    int32_t* bc = at<int32_t>(workspace, p.block_counts);
+    int32_t* bb = at<int32_t>(workspace, p.block_base);
+    LCM_LAUNCH(launch_histogram(s, topk_idx, bc, nullptr, p.nblocks, stream));
+    LCM_LAUNCH(launch_scan(s, bc, p.nblocks, load, offsets, bb, mtiles, n_mtiles, kBmBwd, stream));
+    LCM_LAUNCH(launch_scatter(s, topk_idx, bb, p.nblocks, slot_row, perm_token, stream));
+  }
+  LCM_LAUNCH(launch_ffn_backward(s, p, workspace, x, weights->w_gate, weights->w_up, weights->w_down, topk_idx,
+                                 topk_gate, dy, dx, dw_gate, dw_up, dw_down, stream));
+  return LC_MOE_OK;
+}
+
 lc_moe_status lc_moe_forward(const lc_moe_shape* shape, const void* x,
                              const lc_moe_weights* weights, void* y, int32_t* topk_idx,
                              float* topk_gate, int32_t* load, void* workspace,

@@ -179,6 +179,43 @@ inline bool grids_fit(const lc_moe_shape& s) {
   return f;
 }
 
+// Workspace of lc_moe_ffn_backward (bf16 layers, d and I multiples of 32): the permutation
+// of the given picks (M-tiles of kBmBwd rows), each row's gate, and the row intermediates
+// dH (fp32), g*H, dG, dU (bf16, [T*K][I]) and dX (bf16, [T*K][d]).
+constexpr int kBmBwd = 128;
+struct BwPlan {
+  size_t block_counts, block_base, load, offsets, mtiles, n_mtiles, done, perm_token, slot_row, g_row,
+      dh, gh, dg, du, dxp, total;
+  int nblocks, mt_max;
+};
+inline BwPlan plan_backward(const lc_moe_shape& s) {
+  BwPlan p{};
+  const size_t T = s.T, K = s.K, E = size_t(s.N) + s.Z, N = s.N, tk = T * K;
+  p.nblocks = int((T + kTokBlock - 1) / kTokBlock);
+  size_t mt = N + (tk + kBmBwd - 1) / kBmBwd;
+  if (mt > tk) mt = tk;
+  p.mt_max = int(mt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  p.block_counts = take(size_t(p.nblocks) * E * 4);
+  p.block_base = take(size_t(p.nblocks) * N * 4);
+  p.load = take(E * 4);
+  p.offsets = take((N + 1) * 4);
+  p.mtiles = take(mt * sizeof(MTile));
+  p.n_mtiles = take(4);
+  p.done = take(4);
+  p.perm_token = take(tk * 4);
+  p.slot_row = take(tk * 4);
+  p.g_row = take(tk * 4);
+  p.dh = take(tk * size_t(s.I) * 4);
+  p.gh = take(tk * size_t(s.I) * 2);
+  p.dg = take(tk * size_t(s.I) * 2);
+  p.du = take(tk * size_t(s.I) * 2);
+  p.dxp = take(tk * size_t(s.d) * 2);
+  p.total = o;
+  return p;
+}
+
 // XOR swizzle of the 16-byte chunk slot for 64-byte LDS rows: the 32 rows of one MFMA
 // operand read spread over all banks.
 __host__ __device__ __forceinline__ int swz4(int r) {
@@ -312,6 +349,14 @@ hipError_t launch_quantize_weights(const lc_moe_shape& s, const void* w_gate, co
 //       + (sum of its zero-computation picks' gates, in pick order) * x_t, fp32 accumulation.
 hipError_t launch_combine(const lc_moe_shape& s, const void* x, const void* ybuf,
                           const int32_t* slot_row, const float* gate, void* y, hipStream_t st);
+
+// Backward of the grouped SwiGLU FFN (bf16): from the permutation of the given picks
+// (offsets, M-tile list with kBmBwd-row tiles, perm_token, slot_row) and the picks' gates,
+// writes dx [T][d] and dW_gate, dW_up [N][I][d], dW_down [N][d][I] (bf16).
+hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws, const void* x,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const int32_t* idx, const float* gate, const void* dy, void* dx,
+                               void* dw_gate, void* dw_up, void* dw_down, hipStream_t st);
 
 // One PID update of the selection bias over the E = N+Z experts.
 hipError_t launch_bias_update(int E, long long tk, float kp, float ki, float kd,

@@ -35,22 +35,22 @@ def sigmoid(a: np.ndarray) -> np.ndarray:
         return 1.0 / (1.0 + np.exp(-a))
 
 
-def expert_backward(X, dY, w_gate, w_up, w_down):
+def expert_backward(X, dY, w_gate, w_up, w_down, want_dw=True):
     """One FFN expert on its rows X [m,d] with output gradients dY [m,d] (gates already
-    applied).  Returns (dX [m,d], dW_gate [I,d], dW_up [I,d], dW_down [d,I]), fp64."""
+    applied).  Returns (dX [m,d], dW_gate [I,d], dW_up [I,d], dW_down [d,I]), fp64; the
+    three weight gradients are None when want_dw is False."""
     G = X @ w_gate.T
     U = X @ w_up.T
     s = sigmoid(G)
     a = G * s
     H = a * U
     dH = dY @ w_down
-    dW_down = dY.T @ H
     dG = dH * U * (s + a * (1.0 - s))
     dU = dH * a
-    dW_gate = dG.T @ X
-    dW_up = dU.T @ X
     dX = dG @ w_gate + dU @ w_up
-    return dX, dW_gate, dW_up, dW_down
+    if not want_dw:
+        return dX, None, None, None
+    return dX, dG.T @ X, dU.T @ X, dY.T @ H
 
 
 def ffn_backward(x, dy, idx, gate, experts, N, dw_experts=None):
@@ -79,9 +79,10 @@ def ffn_backward(x, dy, idx, gate, experts, N, dw_experts=None):
             continue
         rows = perm_token[r0:r1]
         wg, wu, wd = experts(e)
-        dX, dWg, dWu, dWd = expert_backward(x[rows], g_row[r0:r1, None] * dy[rows], wg, wu, wd)
+        want = dw_experts is None or e in dw_experts
+        dX, dWg, dWu, dWd = expert_backward(x[rows], g_row[r0:r1, None] * dy[rows], wg, wu, wd, want)
         dX_perm[r0:r1] = dX
-        if dw_experts is None or e in dw_experts:
+        if want:
             dw[e] = (dWg, dWu, dWd)
     dx = np.zeros_like(x)
     for k in range(K):

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -219,3 +219,31 @@ def test_forward_noalloc_validation():
     for T in (64, 128, 256):   # every decode batch of the prefill layer fits
         assert lm.lc_moe_workspace_size(lm.make_shape(T, 6144, 512, 256, 12, 2048, lm.BF16)) <= \
             lm.STATIC_WORKSPACE_BYTES
+
+
+def test_backward_validation():
+    """lc_moe_ffn_backward: bf16 layers with d and I multiples of 32, every pointer needed,
+    a large enough workspace; decided on the host before anything is enqueued."""
+    L = lm.lib()
+    s = good_shape()
+    nb = lm.lc_moe_backward_workspace_size(s)
+    assert nb > 0 and nb % 256 == 0
+    assert lm.lc_moe_backward_workspace_size(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32)) == 0
+    assert lm.lc_moe_backward_workspace_size(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16)) == 0
+    w = lm.Weights(P, P, P, P, P)
+    sp = ctypes.byref(s)
+    args = lambda **kw: [kw.get(k, P) for k in ("x", "idx", "gate", "dy", "dx", "dwg", "dwu", "dwd")]  # noqa: E731
+
+    def call(shape=sp, weights=ctypes.byref(w), ws=P, nbytes=nb, **kw):
+        x, idx, gate, dy, dx, dwg, dwu, dwd = args(**kw)
+        return L.lc_moe_ffn_backward(shape, x, weights, idx, gate, dy, dx, dwg, dwu, dwd, ws, nbytes, None)
+
+    assert call(shape=ctypes.byref(lm.make_shape(64, 128, 8, 4, 2, 256, lm.F32))) == 3
+    assert call(shape=ctypes.byref(lm.make_shape(64, 136, 8, 4, 2, 256, lm.BF16))) == 2
+    assert call(weights=None) == 1
+    assert call(dy=None) == 1
+    assert call(dwd=None) == 1
+    assert call(dx=MIS) == 4
+    assert call(ws=None) == 1
+    assert call(nbytes=nb - 1) == 5
+    assert call(weights=ctypes.byref(lm.Weights(P, P, None, P, P))) == 1

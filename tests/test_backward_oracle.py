@@ -134,15 +134,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
     c = micro(97)
     ref_dx, _ = run(c)
 
-    def wrong_silu_grad(X, dY, wg, wu, wd):  # silu'(G) taken as sigmoid(G)
+    def wrong_silu_grad(X, dY, wg, wu, wd, want_dw=True):  # silu'(G) taken as sigmoid(G)
         G, U = X @ wg.T, X @ wu.T
         s = ob.sigmoid(G)
         dH = dY @ wd
         dG, dU = dH * U * s, dH * G * s
         return dG @ wg + dU @ wu, dG.T @ X, dU.T @ X, dY.T @ (G * s * U)
 
-    def swapped(X, dY, wg, wu, wd):
-        return real(X, dY, wu, wg, wd)
+    def swapped(X, dY, wg, wu, wd, want_dw=True):
+        return real(X, dY, wu, wg, wd, want_dw)
 
     real = ob.expert_backward
     for fn in (wrong_silu_grad, swapped):
