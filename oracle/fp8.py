@@ -17,6 +17,13 @@ format.  Readings taken here:
   * each w / 2^k is rounded to the nearest E4M3 value, ties to the even code;
   * weights only: activations stay bf16, and the layer computed is the bf16 layer with
     every expert weight replaced by its dequantized value code * 2^k.
+FP8 activations too (the FP8 MFMA layer): the pages' DeepSeek-V3 scheme also quantizes
+activations per block; readings taken: blocks of 1 row x 128 reduction columns (the
+DeepSeek-V3 activation tile), the same scale and rounding rules.  The layer then computes
+each FFN expert as G = Q(x) Q(W_gate)^T, U = Q(x) Q(W_up)^T, H = silu(G) * U,
+Y = Q(H) Q(W_down)^T, with Q the block quantization of each operand (x quantized per
+token, H per FFN row), and combines as the bf16 layer (zero-computation experts and the
+router see the unquantized x).
 """
 from __future__ import annotations
 
@@ -117,6 +124,40 @@ def quantize(w):
     ks = np.array([[block_exponent(float(a)) for a in row] for row in amax], np.int64)
     q = (blocks / (2.0 ** ks)[:, None, :, None]).reshape(nrb * BLOCK, ncb * BLOCK)[:R, :C]
     return encode_scaled(q), ks
+
+
+def quantize_rows(a):
+    """Block-FP8 quantization of the rows of a [rows][cols] in blocks of 1 row x 128
+    columns (activations): returns (codes uint8 [rows][cols], k int [rows][ceil(cols/128)])."""
+    a = np.asarray(a, np.float64)
+    R, C = a.shape
+    ncb = -(-C // BLOCK)
+    pad = np.zeros((R, ncb * BLOCK))
+    pad[:, :C] = a
+    blocks = pad.reshape(R, ncb, BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    ks = np.array([[block_exponent(float(v)) for v in row] for row in amax], np.int64)
+    q = (blocks / (2.0 ** ks)[:, :, None]).reshape(R, ncb * BLOCK)[:, :C]
+    return encode_scaled(q), ks
+
+
+def dequantize_rows(codes, ks):
+    """code * 2^k per element for 1 x 128 blocks (fp64; exact)."""
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    ks = np.asarray(ks, np.float64)
+    pad = np.zeros((R, ks.shape[1] * BLOCK))
+    pad[:, :C] = E4M3_TABLE[codes]
+    return (pad.reshape(R, ks.shape[1], BLOCK) * (2.0 ** ks)[:, :, None]).reshape(R, -1)[:, :C]
+
+
+def fp8_act_expert(X, wq_gate, wq_up, wq_down):
+    """One FFN expert of the FP8 MFMA layer on rows X [m,d] (fp64) with dequantized block-FP8
+    weights: Y = Q(H) Q(W_down)^T with H = silu(Q(X) Q(W_gate)^T) * (Q(X) Q(W_up)^T)."""
+    from .moe import silu
+    Xq = dequantize_rows(*quantize_rows(X))
+    H = silu(Xq @ wq_gate.T) * (Xq @ wq_up.T)
+    return dequantize_rows(*quantize_rows(H)) @ wq_down.T
 
 
 def dequantize(codes, ks):

@@ -134,12 +134,15 @@ def moe_forward(x, w_router, bias, experts, N, K, tokens=None):
                                experts, N)[0]
 
 
-def moe_forward_batches(batches, experts, N):
+def moe_forward_batches(batches, experts, N, expert_fn=None):
     """moe_forward of several token batches through one layer's experts (for instance a
     prefill batch and decode batches of the same layer), with one pass over the experts:
     ``experts(e)`` is called once for every expert that any batch routes a token to.
     batches: list of dict(x, w_router, bias, K, tokens=None); returns one moe_forward result
-    per batch, each equal to moe_forward on that batch alone."""
+    per batch, each equal to moe_forward on that batch alone.  expert_fn(X, wg, wu, wd)
+    evaluates one expert on its rows (default swiglu_expert; the FP8 MFMA layer passes
+    oracle.fp8.fp8_act_expert)."""
+    expert_fn = swiglu_expert if expert_fn is None else expert_fn
     prep = []
     for b in batches:
         x = np.asarray(b["x"], np.float64)
@@ -157,7 +160,7 @@ def moe_forward_batches(batches, experts, N):
         for q in prep:
             r0, r1 = q["offsets"][e], q["offsets"][e + 1]
             if r1 > r0:
-                q["y_perm"][r0:r1] = swiglu_expert(q["x"][q["perm_token"][r0:r1]], wg, wu, wd)
+                q["y_perm"][r0:r1] = expert_fn(q["x"][q["perm_token"][r0:r1]], wg, wu, wd)
     out = []
     for q in prep:
         x, idx, gate, slot_row = q["x"], q["idx"], q["gate"], q["slot_row"]

@@ -106,3 +106,54 @@ def test_quantize_planted_mistake_is_caught():
     assert np.any(np.abs(trunc - w) > bound)
     wq = fp8.dequantize(*fp8.quantize(w))
     assert np.all(np.abs(wq - w) <= bound)
+
+
+# ---- activations: 1 x 128 blocks (the FP8 MFMA layer) -----------------------------------
+
+def test_quantize_rows_matches_bruteforce_and_blocks():
+    g = np.random.default_rng(11)
+    x = g.standard_normal((5, 300)) * np.array([[1e-3], [1.0], [30.0], [0.0], [1e4]])
+    x[3, :] = 0.0
+    x[1, 130] = 448.0 * 2 ** -3       # a block maximum exactly on a scale boundary
+    codes, ks = fp8.quantize_rows(x)
+    assert codes.shape == (5, 300) and ks.shape == (5, 3)
+    for r in range(5):
+        for cb in range(3):
+            blk = x[r, cb * 128:(cb + 1) * 128]
+            k = fp8.block_exponent(float(np.abs(blk).max()))
+            assert ks[r, cb] == k
+            for j, v in enumerate(blk):
+                # brute force: the nearest E4M3 value of v / 2^k, ties to the even code
+                t = v / 2.0 ** k
+                vals = fp8.E4M3_TABLE[:0x7F]
+                dist = np.abs(np.abs(t) - vals)
+                best = np.nonzero(dist == dist.min())[0]
+                want = int(best[0]) if best.size == 1 else int(best[best % 2 == 0][0])
+                want |= 0x80 if np.signbit(t) else 0
+                assert codes[r, cb * 128 + j] == want, (r, cb, j, t)
+    assert ks[1, 1] == -3 and codes[1, 130] == 0x7E      # 448 * 2^-3 -> k = -3, code 448
+    assert (ks[3] == 0).all() and (codes[3] == 0).all()
+    np.testing.assert_array_equal(fp8.dequantize_rows(codes, ks)[3], 0.0)
+    # each dequantized value within half an E4M3 step (2^-4 relative for normals) of x
+    d = fp8.dequantize_rows(codes, ks)
+    big = np.abs(x) >= 2.0 ** -6 * 2.0 ** np.repeat(ks, 128, axis=1)[:, :300]
+    assert np.all(np.abs(d - x)[big] <= np.abs(x)[big] * 2 ** -4 + 1e-300)
+
+
+def test_fp8_act_expert_reduces_to_weight_only_on_exact_inputs():
+    """Inputs and H already representable in their block FP8 make the FP8 MFMA expert equal
+    the bf16-activation expert on the same dequantized weights; in general it differs by
+    the activation rounding only (a few % at most)."""
+    from oracle import moe as orc
+    g = np.random.default_rng(12)
+    X = fp8.dequantize_rows(*fp8.quantize_rows(g.standard_normal((7, 256))))
+    wg = fp8.dequantize(*fp8.quantize(g.standard_normal((128, 256)) / 16))
+    wu = fp8.dequantize(*fp8.quantize(g.standard_normal((128, 256)) / 16))
+    wd = fp8.dequantize(*fp8.quantize(g.standard_normal((256, 128)) / 11))
+    np.testing.assert_array_equal(fp8.dequantize_rows(*fp8.quantize_rows(X)), X)   # idempotent
+    a = fp8.fp8_act_expert(X, wg, wu, wd)
+    b = orc.swiglu_expert(X, wg, wu, wd)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert 0 < rel < 0.05              # H's rounding is the only difference left
+    Hq = fp8.dequantize_rows(*fp8.quantize_rows(orc.silu(X @ wg.T) * (X @ wu.T)))
+    np.testing.assert_allclose(a, Hq @ wd.T, rtol=1e-13, atol=1e-15)
