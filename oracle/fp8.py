@@ -151,13 +151,60 @@ def dequantize_rows(codes, ks):
     return (pad.reshape(R, ks.shape[1], BLOCK) * (2.0 ** ks)[:, :, None]).reshape(R, -1)[:, :C]
 
 
+def fp8_act_hidden(X, wq_gate, wq_up):
+    """The first half of one FFN expert of the FP8 MFMA layer on rows X [m,d] (fp64) with
+    dequantized block-FP8 weights: (Q(X), G, U, H) with G = Q(X) Q(W_gate)^T,
+    U = Q(X) Q(W_up)^T, H = silu(G) * U (Q(X) dequantized)."""
+    from .moe import silu
+    Xq = dequantize_rows(*quantize_rows(X))
+    G = Xq @ wq_gate.T
+    U = Xq @ wq_up.T
+    return Xq, G, U, silu(G) * U
+
+
 def fp8_act_expert(X, wq_gate, wq_up, wq_down):
     """One FFN expert of the FP8 MFMA layer on rows X [m,d] (fp64) with dequantized block-FP8
     weights: Y = Q(H) Q(W_down)^T with H = silu(Q(X) Q(W_gate)^T) * (Q(X) Q(W_up)^T)."""
-    from .moe import silu
-    Xq = dequantize_rows(*quantize_rows(X))
-    H = silu(Xq @ wq_gate.T) * (Xq @ wq_up.T)
+    H = fp8_act_hidden(X, wq_gate, wq_up)[3]
     return dequantize_rows(*quantize_rows(H)) @ wq_down.T
+
+
+def rows_requant_bound(a, err):
+    """How far the row quantization of a can move when a is known only to within err.
+
+    a [R][C] (fp64) is quantized in blocks of 1 row x 128 columns (quantize_rows); err [R][C]
+    >= 0 is an absolute uncertainty per element (for instance the rounding error of a
+    computation that produced a in another precision).  Returns delta [R][C] >= 0 with
+    |dequantize_rows(quantize_rows(a'))[i] - dequantize_rows(quantize_rows(a))[i]| <=
+    delta[i] for every a' with |a' - a| <= err elementwise; delta is 0 where neither the
+    element's code nor its block's scale can change.
+      * Block scale: the block maximum of |a'| lies in [lo, hi] (lo = max(|a| - err, 0),
+        hi = max(|a| + err) over the block); if block_exponent(lo) != block_exponent(hi)
+        the scale may change and every element of the block gets the coarse bound
+        err + 2^-3 (|a| + err) + 2^(k_hi - 9): each side is within half an E4M3 step of
+        its input (2^-4 of the value for normals, 2^(k - 10) below them).
+      * Fixed scale 2^k: rounding to the nearest E4M3 value is monotone, so a' / 2^k rounds
+        to a value between the roundings of (a - err) / 2^k and (a + err) / 2^k:
+        delta = 2^k * max distance of those two from the rounding of a / 2^k.
+    """
+    a = np.asarray(a, np.float64)
+    err = np.asarray(err, np.float64)
+    R, C = a.shape
+    ncb = -(-C // BLOCK)
+    pad = lambda m: np.pad(m, ((0, 0), (0, ncb * BLOCK - C))).reshape(R, ncb, BLOCK)  # noqa: E731
+    A, Er = pad(a), pad(err)
+    lo = np.maximum(np.abs(A) - Er, 0.0).max(axis=2)
+    hi = (np.abs(A) + Er).max(axis=2)
+    k0 = np.array([[block_exponent(float(v)) for v in row] for row in np.abs(A).max(axis=2)], np.int64)
+    k_lo = np.array([[block_exponent(float(v)) for v in row] for row in lo], np.int64)
+    k_hi = np.array([[block_exponent(float(v)) for v in row] for row in hi], np.int64)
+    sc = (2.0 ** k0)[:, :, None]
+    fixed = (k_lo == k_hi)[:, :, None] & np.ones_like(A, bool)
+    val = lambda t: E4M3_TABLE[e4m3_encode(np.where(fixed, t, 0.0))]  # noqa: E731
+    q0, q_lo, q_hi = val(A / sc), val((A - Er) / sc), val((A + Er) / sc)
+    delta = np.where(fixed, sc * np.maximum(np.abs(q_hi - q0), np.abs(q_lo - q0)),
+                     Er + 2.0 ** -3 * (np.abs(A) + Er) + (2.0 ** (k_hi - 9))[:, :, None])
+    return delta.reshape(R, ncb * BLOCK)[:, :C]
 
 
 def dequantize(codes, ks):

@@ -157,3 +157,72 @@ def test_fp8_act_expert_reduces_to_weight_only_on_exact_inputs():
     assert 0 < rel < 0.05              # H's rounding is the only difference left
     Hq = fp8.dequantize_rows(*fp8.quantize_rows(orc.silu(X @ wg.T) * (X @ wu.T)))
     np.testing.assert_allclose(a, Hq @ wd.T, rtol=1e-13, atol=1e-15)
+
+
+def test_fp8_act_hidden_is_the_first_half_of_the_expert():
+    from oracle import moe as orc
+    g = np.random.default_rng(13)
+    X = g.standard_normal((5, 256))
+    wg, wu = g.standard_normal((128, 256)) / 16, g.standard_normal((128, 256)) / 16
+    wd = g.standard_normal((256, 128)) / 11
+    Xq, G, U, H = fp8.fp8_act_hidden(X, wg, wu)
+    np.testing.assert_array_equal(Xq, fp8.dequantize_rows(*fp8.quantize_rows(X)))
+    # the expert as a plain SwiGLU block on Q(X), with H quantized before W_down
+    np.testing.assert_allclose(H, orc.swiglu_expert(Xq, wg, wu, np.eye(128)), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(fp8.fp8_act_expert(X, wg, wu, wd),
+                               fp8.dequantize_rows(*fp8.quantize_rows(H)) @ wd.T, rtol=1e-13, atol=1e-15)
+
+
+def _deq_rows(a):
+    return fp8.dequantize_rows(*fp8.quantize_rows(a))
+
+
+def test_rows_requant_bound_zero_uncertainty_and_exact_cases():
+    g = np.random.default_rng(14)
+    a = g.standard_normal((4, 300)) * np.array([[1e-3], [1.0], [30.0], [1e4]])
+    np.testing.assert_array_equal(fp8.rows_requant_bound(a, np.zeros_like(a)), 0.0)
+    # block 0 of row 0: maximum 448 (k = 0); 1.0625 is the midpoint of 1.0 and 1.125, 1.0
+    # is an E4M3 value, 1.03 is 0.03 from the nearest midpoint
+    b = np.zeros((1, 128))
+    b[0, :4] = [448.0, 1.0625, 1.0, 1.03]
+    err = np.zeros_like(b)
+    err[0, 1:4] = 1e-6
+    d = fp8.rows_requant_bound(b, err)
+    assert d[0, 1] == 0.125 and d[0, 2] == 0.0 and d[0, 3] == 0.0 and d[0, 0] == 0.0
+    # the block maximum on the scale boundary 448 * 2^0 with any uncertainty: the scale may
+    # change, so every element of the block is flagged
+    err[0, 0] = 1e-9
+    d = fp8.rows_requant_bound(b, err)
+    assert (d[0] > 0).all()
+
+
+def test_rows_requant_bound_holds_under_brute_force_perturbation():
+    """Definition check: for random rows, uncertainties and perturbations within them (the
+    endpoints included), the requantized values never move by more than the bound."""
+    g = np.random.default_rng(15)
+    R, C = 6, 260
+    a = g.standard_normal((R, C)) * np.exp2(g.integers(-12, 12, (R, 1)))
+    a[0, 5] = 448.0 * 2.0 ** -3                             # a block maximum on a scale boundary
+    a[1, :] = 0.0
+    a[1, 3] = 1e-30
+    mids = (fp8.E4M3_TABLE[1:0x7F] + fp8.E4M3_TABLE[0:0x7E]) / 2     # planted midpoints (k = 0 block)
+    a[2, 128:256] = g.choice(mids, 128) * g.choice([-1.0, 1.0], 128)
+    a[2, 128] = 448.0
+    err = np.abs(a) * 10.0 ** g.uniform(-7, -2, (R, C)) + 1e-40
+    delta = fp8.rows_requant_bound(a, err)
+    q0 = _deq_rows(a)
+    flagged = int((delta > 0).sum())
+    assert 0 < flagged < a.size
+    for t in range(60):
+        if t == 0:
+            s = np.ones_like(a)
+        elif t == 1:
+            s = -np.ones_like(a)
+        else:
+            s = g.choice([-1.0, 1.0, 0.0], a.shape) * (g.uniform(0, 1, a.shape) if t % 2 else 1.0)
+        q = _deq_rows(a + s * err)
+        assert np.all(np.abs(q - q0) <= delta), t
+    # and the bound is reached at planted midpoints: moving across one changes the code
+    moved = _deq_rows(a + err) != q0
+    assert moved[2, 129:256].any()
+
