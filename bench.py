@@ -31,6 +31,8 @@ run on block-FP8 expert weights (fp8_*).
 prefill_packed: the prefill layer on packed bf16 expert weights (lc_moe_pack_weights; at
 this size the same bits as the row-major weights).
 prefill_fp8: the prefill layer on block-FP8 expert weights (lc_moe_quantize_weights).
+prefill_fp8_mfma, skewed.fp8_mfma: the layer on block-FP8 weights and block-FP8 activations
+(lc_moe_weights.fp8_act), both projections on the FP8 matrix cores, against the FP8 peak.
 overlap: a dense SwiGLU FFN (width 2d) over the same tokens beside the layer, serial on one
 stream against concurrent on two streams.
 backward: lc_moe_ffn_backward (dx and every expert's dW) for the forward's picks and a
@@ -51,6 +53,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_gate_up_prefill_T16384_hbm_traffic.txt")
 TRACE_PROFILES = {"prefill": os.path.join(ROOT, "profiles", "ffn_bf16_pipe_kernel_prefill_T16384_kernel_trace.txt"),
@@ -193,6 +196,36 @@ def use_packed(lm, st):
 def drop_packed(lm, st):
     st.pop("packed", None)
     st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"])
+
+
+def fp8_mfma_ok(wl):
+    """Shapes the FP8 MFMA layer takes (bf16, d and I multiples of 64, up to 16384)."""
+    return (wl.dtype == "bf16" and wl.d % 64 == 0 and wl.I % 64 == 0 and wl.d <= 16384 and wl.I <= 16384
+            and wl.T * wl.K * wl.I < 2 ** 31)
+
+
+def fp8_mfma_run(lm, st, wl, steps, warmup, gu_flops, touched):
+    """The layer on block-FP8 weights with FP8 activations (lc_moe_weights.fp8_act): x and H
+    quantized in 1 x 128 blocks, both projections on the FP8 matrix cores.  The gate_up stage
+    includes x's quantization.  Rates against the dense FP8 MFMA peak (5.0 PFLOP/s) and, for
+    comparison with the bf16 layer, the bf16 peak."""
+    st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"], st["fp8"],
+                            None, True)
+    total, stages = run_steps(lm, st, steps, warmup)
+    sm = {k: float(np.mean(v)) for k, v in stages.items()}
+    ffn_ms = sm["gate_up"] + sm["down"]
+    gu_tf = gu_flops / (sm["gate_up"] * 1e-3) / 1e12
+    ffn_tf = 1.5 * gu_flops / (ffn_ms * 1e-3) / 1e12
+    w8 = touched * 3.0 * wl.I * wl.d  # one byte per weight
+    out = {"ms_per_step": total / steps, "tokens_per_s": wl.T * steps / (total * 1e-3), "stages_ms": sm,
+           "gate_up_tflops": gu_tf, "gate_up_fp8_frac": gu_tf / MFMA_FP8_PEAK_TFLOPS,
+           "ffn_ms": ffn_ms, "ffn_tflops": ffn_tf, "ffn_fp8_frac": ffn_tf / MFMA_FP8_PEAK_TFLOPS,
+           "ffn_bf16_frac": ffn_tf / MFMA_BF16_PEAK_TFLOPS, "ffn_weight_GBps": w8 / (ffn_ms * 1e-3) / 1e9}
+    log(f"{wl.name} FP8 MFMA (FP8 weights and activations): {out['ms_per_step']:.3f} ms/step; gate_up "
+        f"{gu_tf:.0f} TFLOP/s ({out['gate_up_fp8_frac']:.1%} of FP8 peak); FFN {ffn_tf:.0f} TFLOP/s "
+        f"({out['ffn_fp8_frac']:.1%} of FP8, {out['ffn_bf16_frac']:.1%} of bf16 peak); stages "
+        f"{json.dumps({k: round(v, 4) for k, v in sm.items()})}")
+    return out
 
 
 def run_steps(lm, st, steps, warmup):
@@ -558,6 +591,8 @@ def main():
                              "gate_up_tflops": gu_flops / (st8["gate_up"] * 1e-3) / 1e12}
     log(f"FP8 weights: {total8 / args.steps:.3f} ms/step; stages "
         f"{json.dumps({k: round(v, 4) for k, v in st8.items()})}")
+    if fp8_mfma_ok(wl):
+        result["prefill_fp8_mfma"] = fp8_mfma_run(lm, st, wl, args.steps, args.warmup, gu_flops, touched)
     st["wts"] = lm._weights(st["wr"], st["b"], st["w"]["gate"], st["w"]["up"], st["w"]["down"])
     if not args.no_backward and wl.dtype == "bf16":
         run_steps(lm, st, 1, 0)  # the row-major forward's picks and gates
@@ -592,6 +627,10 @@ def main():
             log(f"{name}: {xm['ms_per_step']:.3f} ms/step; gate_up {xr['mfma_tflops']:.0f} TFLOP/s "
                 f"({xr['mfma_frac']:.1%}), {xr['hbm_GBps']:.0f} GB/s; FFN {xm['ffn']['TFLOPs']:.0f} TFLOP/s "
                 f"({xm['ffn']['mfma_frac']:.1%}); bound {xr['bound']} at {xr['frac']:.1%}")
+            if fp8_mfma_ok(xw):
+                use_fp8(lm, xst)
+                xm["fp8_mfma"] = fp8_mfma_run(lm, xst, xw, args.steps, args.warmup, xr["flops_per_launch"],
+                                              xm["ffn"]["touched_experts"])
             del xst
             torch.cuda.empty_cache()
     if not args.no_decode:

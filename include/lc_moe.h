@@ -87,6 +87,12 @@ typedef struct {
                             lc_moe_pack_weights; then the FFN reads them instead of
                             w_gate, w_up, w_down (which may be NULL).  At most one of fp8
                             and packed may be set (else LC_MOE_E_DTYPE)                  */
+  int32_t fp8_act;       /* 0, or nonzero with fp8 set: the FFN also quantizes its
+                            activations (x, and H = silu(G) U) to block FP8 in 1 x 128
+                            blocks and multiplies FP8 by FP8 on the matrix cores (see
+                            lc_moe_quantize_activations).  Needs fp8 (else
+                            LC_MOE_E_DTYPE) and d, I multiples of 64 with
+                            T * K * I < 2^31 (else LC_MOE_E_SHAPE)                       */
 } lc_moe_weights;
 
 /* Stages of lc_moe_forward, in launch order (names from lc_moe_stage_name). */
@@ -197,9 +203,10 @@ lc_moe_status lc_moe_forward_noalloc(const lc_moe_shape* shape, const void* x,
  * scale per block of 128 rows x 128 reduction columns of every expert matrix (partial
  * blocks at the edges); the scale is a power of two, 2^k with k the smallest integer such
  * that the block's largest |w| <= 448 * 2^k; each w / 2^k is rounded to the nearest E4M3
- * value, ties to the even code.  Weights only: activations, H and Y stay bf16, and the
- * layer computed is the bf16 layer with every expert weight replaced by code * 2^k (exact
- * in bf16).  Blocks whose scale would fall below 2^-126 (max |w| < 448 * 2^-126) are
+ * value, ties to the even code.  By itself (fp8_act = 0) weights only: activations, H and
+ * Y stay bf16, and the layer computed is the bf16 layer with every expert weight replaced
+ * by code * 2^k (exact in bf16); with fp8_act the activations are quantized too (see
+ * lc_moe_quantize_activations).  Blocks whose scale would fall below 2^-126 (max |w| < 448 * 2^-126) are
  * outside the contract.
  *
  * lc_moe_fp8_weights_size: bytes of the packed form for this shape; 0 when the shape
@@ -213,6 +220,25 @@ size_t lc_moe_fp8_weights_size(const lc_moe_shape* shape);
 lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_gate,
                                       const void* w_up, const void* w_down, void* fp8_weights,
                                       size_t fp8_weights_bytes, hipStream_t stream);
+
+/* Block-FP8 activations (the same section and reading as the weights above, with blocks of
+ * 1 row x 128 columns): the quantizer of lc_moe_weights.fp8_act, which applies it to x and,
+ * inside the FFN, to H.  Each block of 128 consecutive columns of a row (the last one
+ * partial) gets the scale 2^k, k the smallest integer with the block's max |v| <= 448 * 2^k
+ * (k = 0 for an all-zero block), stored as the E8M0 byte k + 127; each v / 2^k rounds to
+ * the nearest E4M3 code, ties to the even code.  The layer computed with fp8_act is then
+ *   G = Q(x) Q(W_gate)^T, U = Q(x) Q(W_up)^T (exact products of dequantized values, fp32
+ *   sums), H = silu(G) U (fp32), Y = Q(H) Q(W_down)^T rounded to bf16,
+ * combined as the bf16 layer's Y is.  Blocks whose max |v| is nonzero but below
+ * 448 * 2^-127 are outside the contract.
+ *   x       [rows][cols] bf16
+ *   codes   [rows][cols] uint8 (out): E4M3 codes
+ *   scales  [rows][ceil(cols / 128)] uint8 (out): E8M0 exponents k + 127
+ * cols a multiple of 64 in [64, 16384], 0 <= rows < 2^24 (else LC_MOE_E_SHAPE); pointers
+ * 16-byte aligned (LC_MOE_E_ALIGN) and non-NULL unless rows = 0 (LC_MOE_E_NULLPTR).
+ * Enqueued on `stream`. */
+lc_moe_status lc_moe_quantize_activations(const void* x, int32_t rows, int32_t cols, void* codes,
+                                          void* scales, hipStream_t stream);
 
 /* Packed bf16 expert weights: the same values as W_gate, W_up [N][I][d] and W_down
  * [N][d][I], re-laid so that every (expert, 128 gate/up or 256 down output columns, 32-wide

@@ -9,9 +9,11 @@ device memory and streams.  The library is opened on first use and a missing bui
 Low-level entry points carry the C names (``lc_moe_route``, ``lc_moe_expert_load``,
 ``lc_moe_permute``, ``lc_moe_forward``, ``lc_moe_forward_staged``, ``lc_moe_forward_noalloc``,
 ``lc_moe_ffn_backward``, ``lc_moe_backward_workspace_size``, ``lc_moe_bias_update``,
-``lc_moe_quantize_weights``, ``lc_moe_fp8_weights_size``, ``lc_moe_pack_weights``,
+``lc_moe_quantize_weights``, ``lc_moe_quantize_activations``, ``lc_moe_fp8_weights_size``,
+``lc_moe_pack_weights``,
 ``lc_moe_packed_weights_size``, ``lc_moe_workspace_size``); ``route``, ``expert_load``,
-``permute``, ``forward``, ``bias_update``, ``quantize_weights`` and ``pack_weights``
+``permute``, ``forward``, ``bias_update``, ``quantize_weights``, ``quantize_activations`` and
+``pack_weights``
 allocate outputs and a workspace with torch where needed and call them.
 """
 from __future__ import annotations
@@ -42,7 +44,8 @@ class Shape(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("fp8", ctypes.c_void_p), ("packed", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("fp8", ctypes.c_void_p), ("packed", ctypes.c_void_p),
+                ("fp8_act", ctypes.c_int32)]
 
 
 class Pid(ctypes.Structure):
@@ -67,6 +70,7 @@ _SIG = {
                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_fp8_weights_size": (_sz, [ctypes.POINTER(Shape)]),
     "lc_moe_quantize_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lc_moe_quantize_activations": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
     "lc_moe_packed_weights_size": (_sz, [ctypes.POINTER(Shape)]),
     "lc_moe_pack_weights": (ctypes.c_int, [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "lc_moe_bias_update": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Pid), _vp, _vp,
@@ -163,9 +167,9 @@ def lc_moe_permute(shape, x, topk_idx, ffn_offsets, perm_token, slot_row, x_perm
            "lc_moe_permute")
 
 
-def _weights(w_router, bias, w_gate, w_up, w_down, fp8=None, packed=None) -> Weights:
+def _weights(w_router, bias, w_gate, w_up, w_down, fp8=None, packed=None, fp8_act=False) -> Weights:
     p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    w = Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8), p(packed))
+    w = Weights(p(w_router), p(bias), p(w_gate), p(w_up), p(w_down), p(fp8), p(packed), int(bool(fp8_act)))
     # the struct holds raw device addresses: keep the tensors alive as long as it lives, or
     # a tensor made inline would go back to torch's allocator and be handed out again
     w._tensors = (w_router, bias, w_gate, w_up, w_down, fp8, packed)
@@ -180,6 +184,11 @@ def lc_moe_quantize_weights(shape, w_gate, w_up, w_down, fp8_weights, stream=Non
     _check(lib().lc_moe_quantize_weights(ctypes.byref(shape), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                         _ptr(fp8_weights), _nbytes(fp8_weights), _stream(stream)),
            "lc_moe_quantize_weights")
+
+
+def lc_moe_quantize_activations(x, rows, cols, codes, scales, stream=None):
+    _check(lib().lc_moe_quantize_activations(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "lc_moe_quantize_activations")
 
 
 def lc_moe_packed_weights_size(shape: Shape) -> int:
@@ -295,10 +304,11 @@ def permute(x, topk_idx, N, E, with_x_perm=True, workspace=None):
 
 
 def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_events=None, fp8=None,
-            packed=None):
+            packed=None, fp8_act=False):
     """dict(y, topk_idx, topk_gate, load); x [T,d]; w_gate/w_up [N,I,d]; w_down [N,d,I];
     fp8: optional block-FP8 weights from quantize_weights (then used instead);
-    packed: optional packed bf16 weights from pack_weights (then read instead)."""
+    packed: optional packed bf16 weights from pack_weights (then read instead);
+    fp8_act: with fp8, quantize x and H to block FP8 too (FP8 matrix cores)."""
     import torch
     N, I, _ = w_gate.shape
     E = w_router.shape[0]
@@ -309,7 +319,7 @@ def forward(x, w_router, bias, w_gate, w_up, w_down, K, workspace=None, stage_ev
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     gate = torch.empty((T, K), dtype=torch.float32, device=dev)
     load = torch.empty(E, dtype=torch.int32, device=dev)
-    wts = _weights(w_router, bias, w_gate, w_up, w_down, fp8, packed)
+    wts = _weights(w_router, bias, w_gate, w_up, w_down, fp8, packed, fp8_act)
     if stage_events is None:
         lc_moe_forward(shape, x, wts, y, idx, gate, load, ws)
     else:
@@ -358,6 +368,19 @@ def quantize_weights(w_gate, w_up, w_down):
     out = torch.empty(n, dtype=torch.uint8, device=w_gate.device)
     lc_moe_quantize_weights(shape, w_gate, w_up, w_down, out)
     return out
+
+
+def quantize_activations(x):
+    """Block-FP8 form of bf16 rows x [rows, cols] (1 x 128 blocks): (codes uint8 [rows, cols],
+    E8M0 scale bytes uint8 [rows, ceil(cols/128)])."""
+    import torch
+    rows, cols = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise TypeError("quantize_activations: x must be a contiguous bf16 tensor")
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, -(-cols // 128)), dtype=torch.uint8, device=x.device)
+    lc_moe_quantize_activations(x, rows, cols, codes, scales)
+    return codes, scales
 
 
 def pack_weights(w_gate, w_up, w_down):

@@ -189,10 +189,12 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   LCM_CHECK(check_ptr(weights->w_router));
   LCM_CHECK(check_ptr(weights->bias));
   if (weights->fp8 && weights->packed) return LC_MOE_E_DTYPE;  // one weight format
+  if (weights->fp8_act && !weights->fp8) return LC_MOE_E_DTYPE;
   if (weights->fp8) {
     LCM_CHECK(check_ptr(weights->fp8));
     if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
     if (plan_fp8(*shape).total == 0) return LC_MOE_E_SHAPE;
+    if (weights->fp8_act && !fp8_mfma_ok(*shape)) return LC_MOE_E_SHAPE;
   } else if (weights->packed) {
     LCM_CHECK(check_ptr(weights->packed));
     if (shape->dtype != LC_MOE_BF16) return LC_MOE_E_DTYPE;
@@ -244,12 +246,20 @@ lc_moe_status lc_moe_forward_staged(const lc_moe_shape* shape, const void* x,
   if (!mark(1)) return LC_MOE_E_DEVICE;
   if (!fused) LCM_CHECK(permute_core(s, idx, p, workspace, ld, offsets, slot_row, perm_token, nullptr, stream));
   if (!mark(2)) return LC_MOE_E_DEVICE;
-  LCM_LAUNCH(launch_ffn_gate_up(s, x, perm_token, weights->w_gate, weights->w_up, weights->fp8,
-                                weights->packed, hbuf, mtiles, offsets, n_mtiles, p.mt_max, stream));
+  if (weights->fp8_act) {  // x quantized, then the FP8 MFMA gate/up (H quantized in it)
+    LCM_LAUNCH(launch_quantize_act(x, s.T, s.d, at<unsigned char>(workspace, p.xq),
+                                   at<unsigned char>(workspace, p.xs), stream));
+    LCM_LAUNCH(launch_ffn_fp8_mfma(s, p, workspace, weights->fp8, 0, stream));
+  } else {
+    LCM_LAUNCH(launch_ffn_gate_up(s, x, perm_token, weights->w_gate, weights->w_up, weights->fp8,
+                                  weights->packed, hbuf, mtiles, offsets, n_mtiles, p.mt_max, stream));
+  }
   if (!mark(3)) return LC_MOE_E_DEVICE;
-  LCM_LAUNCH(launch_ffn_down(s, hbuf, weights->w_down, weights->fp8, weights->packed, ybuf, mtiles,
-                             offsets, n_mtiles,
-                             p.mt_max, stream));
+  if (weights->fp8_act)
+    LCM_LAUNCH(launch_ffn_fp8_mfma(s, p, workspace, weights->fp8, 1, stream));
+  else
+    LCM_LAUNCH(launch_ffn_down(s, hbuf, weights->w_down, weights->fp8, weights->packed, ybuf, mtiles, offsets,
+                               n_mtiles, p.mt_max, stream));
   if (!mark(4)) return LC_MOE_E_DEVICE;
   LCM_LAUNCH(launch_combine(s, x, ybuf, slot_row, gate, y, stream));
   if (!mark(5)) return LC_MOE_E_DEVICE;
@@ -273,6 +283,18 @@ lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_g
   LCM_CHECK(check_ptr(fp8_weights));
   if (fp8_weights_bytes < plan_fp8(*shape).total) return LC_MOE_E_WORKSPACE;
   LCM_LAUNCH(launch_quantize_weights(*shape, w_gate, w_up, w_down, fp8_weights, stream));
+  return LC_MOE_OK;
+}
+
+lc_moe_status lc_moe_quantize_activations(const void* x, int32_t rows, int32_t cols, void* codes,
+                                          void* scales, hipStream_t stream) {
+  if (cols < 64 || cols > 16384 || cols % 64 != 0 || rows < 0 || rows >= (1 << 24)) return LC_MOE_E_SHAPE;
+  if (rows == 0) return LC_MOE_OK;
+  LCM_CHECK(check_ptr(x));
+  LCM_CHECK(check_ptr(codes));
+  LCM_CHECK(check_ptr(scales));
+  LCM_LAUNCH(launch_quantize_act(x, rows, cols, static_cast<unsigned char*>(codes),
+                                 static_cast<unsigned char*>(scales), stream));
   return LC_MOE_OK;
 }
 

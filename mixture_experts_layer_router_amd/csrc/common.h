@@ -105,13 +105,20 @@ inline bool router_fused_split(const lc_moe_shape& s) {
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsPlan {
   size_t logits, wsplit, rpart, idx, gate, block_counts, block_base, load, offsets, mtiles,
-      n_mtiles, done, perm_token, slot_row, hbuf, ybuf, total;
+      n_mtiles, done, perm_token, slot_row, hbuf, ybuf, xq, xs, total;
   int nblocks;  // token blocks of the permutation
   int bm;       // M-tile height for this dtype
   int mt_max;   // capacity of the M-tile list
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Shapes the FP8 MFMA layer takes: 64-element K stages, at most 128 scale blocks per row,
+// and activation matrices (x codes [T][d], H codes [T*K][I]) addressed by 32-bit offsets.
+inline bool fp8_mfma_ok(const lc_moe_shape& s) {
+  return s.dtype == LC_MOE_BF16 && s.d % 64 == 0 && s.I % 64 == 0 && s.d <= 16384 && s.I <= 16384 &&
+         size_t(s.T) * s.K * s.I < (size_t(1) << 31) && size_t(s.T) * s.d < (size_t(1) << 31);
+}
 
 inline WsPlan plan_workspace(const lc_moe_shape& s) {
   WsPlan p{};
@@ -144,6 +151,9 @@ inline WsPlan plan_workspace(const lc_moe_shape& s) {
   p.slot_row = take(tk * 4);
   p.hbuf = take(tk * size_t(s.I) * es);
   p.ybuf = take(tk * size_t(s.d) * es);
+  // the FP8 MFMA layer's x codes and scales (its H codes and scales live in hbuf)
+  p.xq = take(fp8_mfma_ok(s) ? T * size_t(s.d) : 0);
+  p.xs = take(fp8_mfma_ok(s) ? T * size_t((s.d + 127) / 128) : 0);
   p.total = o;
   return p;
 }
@@ -257,6 +267,8 @@ inline Fp8Plan plan_fp8(const lc_moe_shape& s) {
   return p;
 }
 
+// The FP8 MFMA layer (block-FP8 weights and activations): 64-element K stages in both GEMMs.
+
 // bf16 expert weights packed for the pipelined FFN kernel (lc_moe_pack_weights).  Regions
 // (256-byte aligned, in this order):
 //   gu [N][ceil(I/128)][d/32][256 rows][64 B]  rows 0..127 of n-tile nt are W_gate rows
@@ -357,6 +369,17 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
                                const void* w_gate, const void* w_up, const void* w_down,
                                const int32_t* idx, const float* gate, const void* dy, void* dx,
                                void* dw_gate, void* dw_up, void* dw_down, hipStream_t st);
+
+// Block-FP8 activations: rows x cols bf16 (cols a multiple of 64) -> E4M3 codes [rows][cols]
+// and E8M0 scales [rows][ceil(cols/128)] (exponent k + 127 of each 1 x 128 block's 2^k).
+hipError_t launch_quantize_act(const void* x, int rows, int cols, unsigned char* codes,
+                               unsigned char* scales, hipStream_t st);
+// The FP8 MFMA grouped FFN from the x codes and scales in the workspace (p.xq, p.xs) and the
+// block-FP8 weights.  mode 0: gate/up, H quantized in the epilogue into p.hbuf (codes
+// [T*K][I], then E8M0 scales [T*K][ceil(I/128)] at the next 256-byte boundary); mode 1:
+// down, Y rows (bf16) into p.ybuf.
+hipError_t launch_ffn_fp8_mfma(const lc_moe_shape& s, const WsPlan& p, void* ws, const void* fp8, int mode,
+                               hipStream_t st);
 
 // One PID update of the selection bias over the E = N+Z experts.
 hipError_t launch_bias_update(int E, long long tk, float kp, float ki, float kd,

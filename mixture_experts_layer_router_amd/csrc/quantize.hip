@@ -6,30 +6,9 @@
 // code.  The codes are written straight into the packed pair-row layout the FFN kernel
 // streams (see Fp8Plan), the scales as fp32 powers of two.
 #include "common.h"
+#include "fp8.h"
 
 namespace lcm {
-
-// Nearest E4M3 code of v (finite, |v| <= 448), ties to even; sign bit from v.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  uint32_t q;
-  if (a < 0.015625f) {                         // below 2^-6: subnormal steps of 2^-9
-    q = static_cast<uint32_t>(rintf(a * 512.f));  // 0..8 (8 is the smallest normal)
-  } else {
-    const int e = ilogbf(a);                   // -6..8
-    const float m = ldexpf(a, -e);             // [1, 2), exact
-    q = static_cast<uint32_t>((e + 7) << 3) + static_cast<uint32_t>(rintf((m - 1.f) * 8.f));
-  }
-  return q | sign;
-}
-
-// Smallest k with amax <= 448 * 2^k (0 for amax == 0); 448 = 1.75 * 2^8.
-__device__ __forceinline__ int block_exp(float amax) {
-  if (amax == 0.f) return 0;
-  const int e = ilogbf(amax);
-  return ldexpf(amax, -e) <= 1.75f ? e - 8 : e - 7;
-}
 
 // One workgroup per 128x128 block of one matrix: blockIdx = (column block, row block,
 // expert * nmat + matrix).  MAT_GU: matrices 0 (gate) and 1 (up) of [N][I][d]; else

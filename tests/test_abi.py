@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     lib = lm.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -168,6 +168,27 @@ def test_forward_weight_format_validation():
                             lm.lc_moe_workspace_size(odd), None) == 2
     mis = lm.Weights(P, P, None, None, None, None, MIS)
     assert L.lc_moe_forward(sp, P, ctypes.byref(mis), P, None, None, None, P, nb, None) == 4
+    # FP8 activations need the FP8 weights, and d, I multiples of 64
+    act_only = lm.Weights(P, P, P, P, P, None, None, 1)
+    assert L.lc_moe_forward(sp, P, ctypes.byref(act_only), P, None, None, None, P, nb, None) == 3
+    act = lm.Weights(P, P, None, None, None, P, None, 1)
+    d96 = lm.make_shape(64, 96, 8, 4, 2, 256, lm.BF16)     # d % 32 == 0 (FP8 weights) but d % 64 != 0
+    assert lm.lc_moe_fp8_weights_size(d96) > 0
+    assert L.lc_moe_forward(ctypes.byref(d96), P, ctypes.byref(act), P, None, None, None, P,
+                            lm.lc_moe_workspace_size(d96), None) == 2
+
+
+def test_quantize_activations_validation():
+    f = lm.lib().lc_moe_quantize_activations
+    assert f(P, 4, 96, P, P, None) == 2          # cols % 64
+    assert f(P, 4, 0, P, P, None) == 2
+    assert f(P, 4, 16384 + 64, P, P, None) == 2
+    assert f(P, -1, 128, P, P, None) == 2
+    assert f(P, 1 << 24, 128, P, P, None) == 2
+    assert f(None, 4, 128, P, P, None) == 1
+    assert f(P, 4, 128, P, None, None) == 1
+    assert f(P, 4, 128, MIS, P, None) == 4
+    assert f(None, 0, 128, None, None, None) == 0  # nothing to do
 
 
 
