@@ -36,30 +36,46 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// One wave per 128-column block of one row: lane l takes columns 2l, 2l+1.  cols is a
-// multiple of 64, so a lane's two columns are both in or both out.
+// 16 lanes per 128-column block of one row, 8 columns (one 16-byte load) per lane; the
+// blocks of a row are consecutive 16-lane groups, so a group never straddles two rows.  cols
+// is a multiple of 64: in a last block of 64 columns the upper 8 lanes hold nothing.
 __global__ __launch_bounds__(256) void quantize_act_kernel(const bf16_t* __restrict__ x,
                                                            unsigned char* __restrict__ codes,
                                                            unsigned char* __restrict__ scales,
                                                            int rows, int cols, int nkb) {
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (w >= rows * nkb) return;  // whole waves
-  const int r = w / nkb, cb = w - r * nkb;
-  const int c = cb * 128 + lane * 2;
-  float v0 = 0.f, v1 = 0.f;
-  if (c < cols) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(x + size_t(r) * cols + c);
-    v0 = bf2f(bf16_t(u & 0xFFFF));
-    v1 = bf2f(bf16_t(u >> 16));
-  }
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  const size_t t = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const size_t per_row = size_t(nkb) * 16;
+  const bool live = t < size_t(rows) * per_row;  // whole 16-lane groups live or not
+  const int r = live ? int(t / per_row) : 0;
+  const int j = int(t - size_t(r) * per_row), cb = j >> 4;
+  const int c = cb * 128 + (j & 15) * 8;
+  const bool in = live && c < cols;
+  float v[8];
+  float amax = 0.f;
+  if (in) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + size_t(r) * cols + c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf2f(bf16_t(w[q] & 0xFFFF));
+      v[2 * q + 1] = bf2f(bf16_t(w[q] >> 16));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));  // within the group
   const int k = block_exp(amax);
-  if (c < cols)
-    *reinterpret_cast<uint16_t*>(codes + size_t(r) * cols + c) =
-        uint16_t(e4m3_code(ldexpf(v0, -k)) | (e4m3_code(ldexpf(v1, -k)) << 8));
-  if (lane == 0) scales[size_t(r) * nkb + cb] = static_cast<unsigned char>(k + 127);
+  if (in) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo |= e4m3_code(ldexpf(v[q], -k)) << (8 * q);
+      hi |= e4m3_code(ldexpf(v[q + 4], -k)) << (8 * q);
+    }
+    *reinterpret_cast<uint2*>(codes + size_t(r) * cols + c) = make_uint2(lo, hi);
+  }
+  if (live && (j & 15) == 0) scales[size_t(r) * nkb + cb] = static_cast<unsigned char>(k + 127);
 }
 
 // Map a workgroup to (M-tile j, n-tile), as the pipelined bf16 kernel does.
@@ -123,15 +139,21 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
   // Every LDS read in the K loop uses a bf16 vector or bf16 type, like the direct loads' LDS
   // writes are seen by the compiler's type-based alias analysis; reads of other types made
   // it wait for every load in flight first.  So the scales are kept as 16-bit slots.
-  // Layout [K block][row]: a row block's scales sit at a fixed offset from the first's.
-  const int sc_bytes = (BM * nkb * 2 + 1023) & ~1023;
+  // Layout [K block][row pair], the scale bytes of rows 2p and 2p+1 in one 16-bit slot: a row
+  // block's slots sit at a fixed offset from the first's, and the table takes half the LDS of
+  // one slot per row (four ring stages at d = 6144 instead of three).
+  const int sc_bytes = (BM * nkb + 1023) & ~1023;
   __bf16* sc = reinterpret_cast<__bf16*>(smem + LDS_BYTES - sc_bytes);
-  for (int i = tid; i < BM * nkb; i += 512) {
-    const int kb = i / BM, r = i - kb * BM;
-    uint16_t v = 127;
+  for (int i = tid; i < (BM / 2) * nkb; i += 512) {
+    const int kb = i / (BM / 2), r = 2 * (i - kb * (BM / 2));
+    uint16_t v = 127 | (127 << 8);
     if (r < rows) {
-      const size_t src_row = MODE == 0 ? size_t(perm_token[row0 + r]) : size_t(row0 + r);
-      v = a_scales[src_row * nkb + kb];
+      const size_t s0 = MODE == 0 ? size_t(perm_token[row0 + r]) : size_t(row0 + r);
+      v = (v & 0xFF00) | a_scales[s0 * nkb + kb];
+    }
+    if (r + 1 < rows) {
+      const size_t s1 = MODE == 0 ? size_t(perm_token[row0 + r + 1]) : size_t(row0 + r + 1);
+      v = (v & 0x00FF) | (uint16_t(a_scales[s1 * nkb + kb]) << 8);
     }
     sc[i] = __builtin_bit_cast(__bf16, v);
   }
@@ -216,19 +238,23 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
       const i32x4 lo = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(st + a_lo + mb * 64 * RB));
       const i32x4 hi = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(st + a_hi + mb * 64 * RB));
       fa[buf] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      sa[buf] = __builtin_bit_cast(uint16_t, sc[kb * BM + wm * 32 + l32 + mb * 64]);
+      sa[buf] = (__builtin_bit_cast(uint16_t, sc[kb * (BM / 2) + ((wm * 32 + l32) >> 1) + mb * 32]) >> (8 * (l32 & 1))) &
+                0xFF;
     };
-    // B fragments (the lane's pair row, both halves) and their scales
+    // B fragments (the lane's pair row, both halves) and their scales: one 16-byte read per
+    // 8-element K group holds both halves' 8 bytes.  Lanes l and l + 16 read the same banks,
+    // but a 16-byte read serves a quarter wave at a time, whose 16 lanes hit 16 distinct
+    // 16-byte bank groups (row bits 0..1 and the swizzle of bits 2..3).
     auto rd_b = [&](const unsigned char* st, int kb) {
       const unsigned char* bb = st + a_bytes + h * 8192 + bp * 64;
       const int swb = swz4(bp);
+      i32x4 p[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) p[g] = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(bb + ((g ^ swb) << 4)));
+      fb[0] = i32x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+      fb[1] = i32x8{p[0][2], p[0][3], p[1][2], p[1][3], p[2][2], p[2][3], p[3][2], p[3][3]};
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        i32x2 p[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          p[g] = __builtin_bit_cast(i32x2, *reinterpret_cast<const bf16x4*>(bb + ((g ^ swb) << 4) + nb * 8));
-        fb[nb] = i32x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
         const int v = kb < 64 ? vsc[nb][0] : vsc[nb][1];
         sb[nb] = __builtin_amdgcn_readlane(v, kb & 63);
       }
@@ -368,8 +394,8 @@ Fp8MfmaKernel fp8_mfma_kernel(const lc_moe_shape& s) {
 hipError_t launch_quantize_act(const void* x, int rows, int cols, unsigned char* codes,
                                unsigned char* scales, hipStream_t st) {
   const int nkb = (cols + 127) / 128;
-  const size_t waves = size_t(rows) * nkb;
-  hipLaunchKernelGGL(quantize_act_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, st,
+  const size_t threads = size_t(rows) * nkb * 16;
+  hipLaunchKernelGGL(quantize_act_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, st,
                      static_cast<const bf16_t*>(x), codes, scales, rows, cols, nkb);
   return hipGetLastError();
 }
