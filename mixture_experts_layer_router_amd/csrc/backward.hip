@@ -30,8 +30,11 @@ namespace lcm {
 namespace bw {
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDR = BK + 8;    // row tile: [128][40] bf16 (80-byte rows)
-constexpr int LDC = BM + 8;    // col tile: [32][136] bf16 (272-byte rows)
-constexpr int TILE = BM * LDR; // elements per operand and stage (the larger of the two forms)
+// col tile: [32][160] bf16 (320-byte rows: a transposing read's four 16-lane groups read
+// rows 16 dwords apart, 32 bytes each, on 64 distinct banks)
+constexpr int LDC = BM + 32;
+constexpr int TILE = BM * LDR; // elements per operand and stage (both forms: 128 x 40 = 32 x 160)
+static_assert(BK * LDC <= TILE, "col tile must fit the stage");
 enum { DH = 0, GU = 1, DX = 2, DWD = 3, DWGU = 4 };
 }  // namespace bw
 
@@ -195,13 +198,22 @@ __global__ __launch_bounds__(256, 2) void ffn_backward_kernel(BwArgs a) {
   // tile rows of the wave's two A blocks and two B blocks
   const int am[2] = {wm * 64, wm * 64 + 32};
   const int bn[2] = {KIND == GU ? wn * 32 : wn * 64, KIND == GU ? 64 + wn * 32 : wn * 64 + 32};
-  // fragment of one 32-row block at k offset kk: 8 consecutive k of row (base + lane % 32)
+  // fragment of one 32-row block at k offset kk: 8 consecutive k of row (base + lane % 32).
+  // A col tile holds [k][m]; gfx950's transposing LDS read (ds_read_b64_tr_b16) gives lane
+  // 16g + 4a + b element b of the 8 bytes addressed by lanes 16g + 4j + a, j = 0..3, as its
+  // element j.  So lane 16g + 4j + a points at k row kk + 8 (g / 2) + 4 h + j, m column
+  // base + 16 (g % 2) + 4 a: two reads (h = 0, 1) give the lane's 8 k values of row
+  // base + lane % 32.
+  const int tr_k = 8 * (lane >> 5) + ((lane >> 2) & 3), tr_m = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   auto frag = [&](const bf16_t* tile, bool colform, int base, int kk) -> bf16x8 {
     if (!colform) return *reinterpret_cast<const bf16x8*>(tile + (base + lr) * LDR + kk + lk);
-    bf16x8 v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(__bf16, tile[(kk + lk + j) * LDC + base + lr]);
-    return v;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const bf16_t* p = tile + (kk + tr_k) * LDC + base + tr_m;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * LDC));
+    return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                                hi[0], hi[1], hi[2], hi[3]});
   };
 
   f32x16 acc[2][2];
