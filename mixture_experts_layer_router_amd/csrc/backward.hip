@@ -64,7 +64,7 @@ struct BwArgs {
 };
 
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void ffn_backward_kernel(BwArgs a) {
+__global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
   using namespace bw;
   constexpr bool A_COL = KIND == DWD || KIND == DWGU;
   constexpr bool B_COL = KIND != GU;

@@ -67,7 +67,10 @@ def check(case, idx, gate32, out, dy, dw_experts=None):
 
 
 CASES = [dict(T=300, d=256, N=12, Z=5, K=4, I=192), dict(T=64, d=128, N=8, Z=4, K=3, I=96),
-         dict(T=700, d=160, N=6, Z=3, K=3, I=96), dict(T=257, d=64, N=9, Z=0, K=2, I=64)]
+         dict(T=700, d=160, N=6, Z=3, K=3, I=96), dict(T=257, d=64, N=9, Z=0, K=2, I=64),
+         # experts of about 500 rows (four 128-row M-tiles, the last ragged); d and I past
+         # two 128-wide tiles, both ragged
+         dict(T=1500, d=320, N=4, Z=2, K=3, I=288)]
 
 
 @pytest.mark.parametrize("kw", CASES, ids=lambda k: f"T{k['T']}_d{k['d']}_I{k['I']}_Z{k['Z']}")
