@@ -7,13 +7,14 @@
 // For the rows r of FFN expert e (pick (t, k) with gate g, x_r = x_t, dy_r = dy_t):
 //   G = x_r W_gate^T, U = x_r W_up^T, s = sigmoid(G), a = G s, H = a U
 //   dH_r   = g dy_r W_down                      (kind DH)
-//   gH_r   = g H_r;  dG_r = dH_r U (s + a (1 - s));  dU_r = dH_r a     (kind GU: G, U recomputed)
+//   gH_r   = g H_r;  dG_r = dH_r U (s + a (1 - s));  dU_r = dH_r a     (G and U recomputed by
+//            the forward's pipelined gate/up kernel with its backward epilogue, ffn.hip MODE 2)
 //   dX_r   = dG_r W_gate + dU_r W_up            (kind DX)
 //   dW_down_e = sum_r dy_r^T gH_r               (kind DWD)
 //   dW_gate_e = sum_r dG_r^T x_r, dW_up_e = sum_r dU_r^T x_r        (kind DWGU)
 //   dx_t = sum over the token's FFN picks, in pick order, of dX_r + (zero picks' gate sum) dy_t
 //
-// All five products run on one grouped GEMM kernel, C[m][n] = sum_k A(m, k) B(n, k), bf16 on
+// The other four products run on one grouped GEMM kernel, C[m][n] = sum_k A(m, k) B(n, k), bf16 on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Each operand is either K-contiguous
 // ("row": element (m, k) at row m, column k, as the forward's weights and activations) or
 // M-contiguous ("col": for a fixed k the m run contiguously, as W_down read along its
@@ -35,7 +36,7 @@ constexpr int LDR = BK + 8;    // row tile: [128][40] bf16 (80-byte rows)
 constexpr int LDC = BM + 32;
 constexpr int TILE = BM * LDR; // elements per operand and stage (both forms: 128 x 40 = 32 x 160)
 static_assert(BK * LDC <= TILE, "col tile must fit the stage");
-enum { DH = 0, GU = 1, DX = 2, DWD = 3, DWGU = 4 };
+enum { DH = 0, DX = 2, DWD = 3, DWGU = 4 };  // (1: G/U, on the pipelined gate/up kernel)
 }  // namespace bw
 
 struct BwArgs {
@@ -66,14 +67,13 @@ struct BwArgs {
 template <int KIND>
 __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
   using namespace bw;
-  constexpr bool A_COL = KIND == DWD || KIND == DWGU;
-  constexpr bool B_COL = KIND != GU;
+  constexpr bool A_COL = KIND == DWD || KIND == DWGU;  // B is M-contiguous in every kind
   __shared__ __attribute__((aligned(16))) bf16_t As[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][TILE];
 
   // ---- the work unit ------------------------------------------------------------------
   int e, mrows, m0 = 0, n0, ktot, row0 = 0, mat = 0;
-  if constexpr (KIND == DH || KIND == GU || KIND == DX) {
+  if constexpr (KIND == DH || KIND == DX) {
     // (M-tile of an expert's rows, N-tile); XCD-aware order as in the forward
     const int nmt = *a.n_mtiles, U = nmt * a.n_ntiles, per = (U + 7) >> 3;
     const int slot = blockIdx.x >> 3;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
     e = t.expert;
     row0 = t.row0;
     mrows = t.rows;
-    n0 = nt * (KIND == GU ? BN / 2 : BN);
+    n0 = nt * BN;
     ktot = KIND == DX ? 2 * a.I : a.d;
   } else {
     // (expert, matrix, M-tile, N-tile), expert-major; K = the expert's rows
@@ -109,14 +109,13 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
     ktot = a.offsets[e + 1] - row0;
     mrows = (KIND == DWD ? a.d : a.I) - m0;
   }
-  const int ncols = KIND == DH ? a.I : KIND == GU ? a.I : KIND == DX ? a.d : KIND == DWD ? a.I : a.d;
+  const int ncols = KIND == DH ? a.I : KIND == DX ? a.d : KIND == DWD ? a.I : a.d;
   const int tid = threadIdx.x;
 
   // ---- load assignment ----------------------------------------------------------------
   // row tile: chunk q = tid + 256 i (i < 2): row q / 4, k offset (q % 4) * 8
   // col tile: chunk q: line k = q / 16, m offset (q % 16) * 8
   const bf16_t* arow[2] = {nullptr, nullptr};
-  const bf16_t* brow[2] = {nullptr, nullptr};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = tid + 256 * i;
@@ -125,14 +124,8 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
       if (r < mrows) {
         const size_t grow = size_t(row0 + r);
         if (KIND == DH) arow[i] = a.dy + size_t(a.perm_token[grow]) * a.d;
-        else if (KIND == GU) arow[i] = a.x + size_t(a.perm_token[grow]) * a.d;
         else arow[i] = a.dg + grow * a.I;  // DX: dG for k < I, dU after (switched below)
       }
-    }
-    if constexpr (!B_COL) {  // GU: B rows 0..63 gate rows n0.., 64..127 up rows n0..
-      const int r = q >> 2;
-      const int c = n0 + (r & 63);
-      if (c < a.I) brow[i] = (r < 64 ? a.wg : a.wu) + (size_t(e) * a.I + c) * a.d;
     }
   }
   uint4 ra[2], rb[2];
@@ -170,10 +163,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
                                         : make_uint4(0, 0, 0, 0);
       }
       // B
-      if constexpr (!B_COL) {
-        const int kc = (q & 3) * 8;
-        rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
-      } else {
+      {
         const int k = k0 + (q >> 4), nc = (q & 15) * 8;
         rb[i] = (k < ktot && nc < nlim) ? *reinterpret_cast<const uint4*>(line_ptr(1, k) + nc)
                                         : make_uint4(0, 0, 0, 0);
@@ -186,8 +176,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
       const int q = tid + 256 * i;
       if constexpr (!A_COL) *reinterpret_cast<uint4*>(&As[buf][(q >> 2) * LDR + (q & 3) * 8]) = ra[i];
       else *reinterpret_cast<uint4*>(&As[buf][(q >> 4) * LDC + (q & 15) * 8]) = ra[i];
-      if constexpr (!B_COL) *reinterpret_cast<uint4*>(&Bs[buf][(q >> 2) * LDR + (q & 3) * 8]) = rb[i];
-      else *reinterpret_cast<uint4*>(&Bs[buf][(q >> 4) * LDC + (q & 15) * 8]) = rb[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][(q >> 4) * LDC + (q & 15) * 8]) = rb[i];
     }
   };
 
@@ -197,7 +186,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   // tile rows of the wave's two A blocks and two B blocks
   const int am[2] = {wm * 64, wm * 64 + 32};
-  const int bn[2] = {KIND == GU ? wn * 32 : wn * 64, KIND == GU ? 64 + wn * 32 : wn * 64 + 32};
+  const int bn[2] = {wn * 64, wn * 64 + 32};
   // fragment of one 32-row block at k offset kk: 8 consecutive k of row (base + lane % 32).
   // A col tile holds [k][m]; gfx950's transposing LDS read (ds_read_b64_tr_b16) gives lane
   // 16g + 4a + b element b of the 8 bytes addressed by lanes 16g + 4j + a, j = 0..3, as its
@@ -238,7 +227,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) fa[i] = frag(As[buf], A_COL, am[i], ks);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = frag(Bs[buf], B_COL, bn[j], ks);
+        for (int j = 0; j < 2; ++j) fb[j] = frag(Bs[buf], true, bn[j], ks);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -257,18 +246,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int m = am[i] + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (m >= mrows) continue;
-      if constexpr (KIND == GU) {
-        const int col = n0 + wn * 32 + lr;
-        if (col >= a.I) continue;
-        const size_t o = size_t(row0 + m) * a.I + col;
-        const float G = acc[i][0][r], U = acc[i][1][r];
-        const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-G * 1.4426950408889634f));
-        const float act = G * s;
-        const float dh = a.dh[o], g = a.g_row[row0 + m];
-        a.gh[o] = f2bf(g * (act * U));
-        a.dg[o] = f2bf(dh * U * (s + act * (1.f - s)));
-        a.du[o] = f2bf(dh * act);
-      } else {
+      {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = n0 + bn[j] + lr;
@@ -378,8 +356,14 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
   // activation kinds: units over the M-tile list
   a.n_ntiles = (s.I + BN - 1) / BN;
   hipLaunchKernelGGL(ffn_backward_kernel<DH>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
-  a.n_ntiles = (s.I + BN / 2 - 1) / (BN / 2);
-  hipLaunchKernelGGL(ffn_backward_kernel<GU>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
+  // G and U recomputed on the forward's pipelined gate/up kernel (its own M-tile height)
+  MTile* pipe_mtiles = reinterpret_cast<MTile*>(w + p.pipe_mtiles);
+  int32_t* pipe_n = reinterpret_cast<int32_t*>(w + p.pipe_n_mtiles);
+  hipError_t err = launch_mtile_list(s, a.offsets, p.pipe_bm, pipe_mtiles, pipe_n, st);
+  if (err != hipSuccess) return err;
+  err = launch_ffn_gate_up_grad(s, x, a.perm_token, w_gate, w_up, GuGrad{a.dh, a.g_row, a.dg, a.du}, a.gh,
+                                pipe_mtiles, a.offsets, pipe_n, p.pipe_mt_max, st);
+  if (err != hipSuccess) return err;
   a.n_ntiles = (s.d + BN - 1) / BN;
   hipLaunchKernelGGL(ffn_backward_kernel<DX>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
   // weight kinds: every expert (an expert without rows gets zero gradients)

@@ -195,8 +195,9 @@ inline bool grids_fit(const lc_moe_shape& s) {
 constexpr int kBmBwd = 128;
 struct BwPlan {
   size_t block_counts, block_base, load, offsets, mtiles, n_mtiles, done, perm_token, slot_row, g_row,
-      dh, gh, dg, du, dxp, total;
+      dh, gh, dg, du, dxp, pipe_mtiles, pipe_n_mtiles, total;
   int nblocks, mt_max;
+  int pipe_bm, pipe_mt_max;  // the M-tile list of the pipelined gate/up kernel's recompute
 };
 inline BwPlan plan_backward(const lc_moe_shape& s) {
   BwPlan p{};
@@ -222,6 +223,13 @@ inline BwPlan plan_backward(const lc_moe_shape& s) {
   p.dg = take(tk * size_t(s.I) * 2);
   p.du = take(tk * size_t(s.I) * 2);
   p.dxp = take(tk * size_t(s.d) * 2);
+  // G and U are recomputed by the forward's pipelined gate/up kernel, on its own tile height
+  p.pipe_bm = ffn_small(s) ? kBmSmall : kBmPipe;
+  size_t mt2 = N + (tk + p.pipe_bm - 1) / p.pipe_bm;
+  if (mt2 > tk) mt2 = tk;
+  p.pipe_mt_max = int(mt2);
+  p.pipe_mtiles = take(mt2 * sizeof(MTile));
+  p.pipe_n_mtiles = take(4);
   p.total = o;
   return p;
 }
@@ -374,6 +382,24 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
 // and E8M0 scales [rows][ceil(cols/128)] (exponent k + 127 of each 1 x 128 block's 2^k).
 hipError_t launch_quantize_act(const void* x, int rows, int cols, unsigned char* codes,
                                unsigned char* scales, hipStream_t st);
+// The pipelined gate/up kernel's backward form (MODE 2): G and U recomputed for the rows of
+// an M-tile list of the pipelined kernel's height; with dH (fp32 [rows][I]) and each FFN row's
+// gate g it writes g*H into gh and dG, dU (bf16 [rows][I]).
+struct GuGrad {
+  const float* dh;
+  const float* g_row;
+  bf16_t* dg;
+  bf16_t* du;
+};
+hipError_t launch_ffn_gate_up_grad(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
+                                   const void* w_gate, const void* w_up, const GuGrad& gg, void* gh,
+                                   const MTile* mtiles, const int32_t* offsets, const int32_t* n_mtiles,
+                                   int mt_max, hipStream_t st);
+// An M-tile list of height bm over the FFN experts' rows given by offsets [N+1] (one
+// workgroup; the same tiles the permutation's scan would list at that height).
+hipError_t launch_mtile_list(const lc_moe_shape& s, const int32_t* offsets, int bm, MTile* mtiles,
+                             int32_t* n_mtiles, hipStream_t st);
+
 // The FP8 MFMA grouped FFN from the x codes and scales in the workspace (p.xq, p.xs) and the
 // block-FP8 weights.  mode 0: gate/up, H quantized in the epilogue into p.hbuf (codes
 // [T*K][I], then E8M0 scales [T*K][ceil(I/128)] at the next 256-byte boundary); mode 1:

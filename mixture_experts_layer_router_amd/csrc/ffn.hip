@@ -4,6 +4,8 @@
 //
 //   gate/up:  H[r] = silu(W_gate,e x_t) * (W_up,e x_t)    for row r of expert e, t = perm_token[r]
 //   down:     Y[r] = W_down,e H[r]
+// MODE 0 is gate/up, MODE 1 down; MODE 2 is gate/up with the backward epilogue of the FFN's
+// gradient (G and U recomputed; g*H, dG and dU written from dH and the row's gate).
 //
 // Work unit = (M-tile of one expert, n-tile of output columns).  The M-tile list is built
 // on the device by the scan kernel, so the host never learns the per-expert row counts;
@@ -270,8 +272,9 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
     const unsigned char* __restrict__ qcodes, const float* __restrict__ qscales, int nrb_rows,
     int nkb, bf16_t* __restrict__ out, const MTile* __restrict__ mtiles,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_mtiles_ptr, int kdim,
-    int ncols, int n_ntiles, int bpacked) {
+    int ncols, int n_ntiles, int bpacked, GuGrad gg) {
   constexpr int BM = SMALL ? kBmSmall : kBmPipe;  // 64 / 320
+  constexpr bool GATE_UP = MODE != 1;               // MODE 0 forward, MODE 2 backward recompute
   constexpr int BK = 32;                  // K step
   constexpr int LDS_BYTES = (SMALL ? 80 : 160) * 1024;  // the ring
   constexpr int MAX_NST = 16;             // ring stages at most
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
   if (!unit_of_block(mtiles, offsets, *n_mtiles_ptr, n_ntiles, BM, j, ntile)) return;
   const MTile tile = mtiles[j];
   const int e = tile.expert, row0 = tile.row0, rows = tile.rows;
-  const int n0 = ntile * (MODE == 0 ? 128 : 256);
+  const int n0 = ntile * (GATE_UP ? 128 : 256);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
     const int r = q * RPI + lrow;
     na += (q < NIA && q * RPI < rows) ? 1 : 0;
     const int ar = r < rows ? r : 0;  // rows past the tile read a valid row; never stored
-    const size_t src_row = MODE == 0 ? size_t(perm_token[row0 + ar]) : size_t(row0 + ar);
+    const size_t src_row = GATE_UP ? size_t(perm_token[row0 + ar]) : size_t(row0 + ar);
     srcA[i] = a_src + src_row * kdim + (lslot ^ swz4(r)) * 8;
   }
   // FP8: weight load q is the 1 KB piece q of the stage's 8 KB tile block, copied as is.
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
       const int r = (wave + 8 * i) * RPI + lrow;  // weight row of the tile, 0..255
       int c;
       const bf16_t* mat;
-      if (MODE == 0) {
+      if (GATE_UP) {
         c = n0 + (r & 127);
         mat = r < 128 ? w0 : w1;
       } else {
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
     boff[nb] = a_bytes + (FP8 ? (wn * 32 + l32) * 64  // FP8: pair-row wn*32 + l32 holds both blocks
-                              : ((MODE == 0 ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + l32) * RB);
+                              : ((GATE_UP ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + l32) * RB);
   // FP8 scales of the wave's two weight blocks (the rows of one 32-row weight block lie in
   // one 128-row block): lane l holds the scale of column block l in vsc[nb][0] and of
   // column block 64 + l in vsc[nb][1] (nkb <= 128), loaded once before the loads start;
@@ -560,6 +563,24 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
         if (row < rows)
           out[size_t(row0 + row) * ncols + col] = f2bf(swiglu_fast(acc[mb][0][r], acc[mb][1][r]));
       }
+    } else if (MODE == 2) {
+      // backward of the SwiGLU (s = sigmoid(G), a = G s): g*H = g a U, dG = dH U (s + a (1 - s)),
+      // dU = dH a, each rounded to bf16
+      const int col = n0 + wn * 32 + l32;
+      if (col >= ncols) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (mb * 2 + wm) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row >= rows) continue;
+        const size_t o = size_t(row0 + row) * ncols + col;
+        const float G = acc[mb][0][r], U = acc[mb][1][r];
+        const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-G * 1.4426950408889634f));
+        const float act = G * sg;
+        const float dh = gg.dh[o], g = gg.g_row[row0 + row];
+        out[o] = f2bf(g * (act * U));
+        gg.dg[o] = f2bf(dh * U * (sg + act * (1.f - sg)));
+        gg.du[o] = f2bf(dh * act);
+      }
     } else {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -580,7 +601,9 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_bf16_pipe_kernel(
       const bf16_t* __restrict__, const int32_t* __restrict__, const bf16_t* __restrict__,    \
       const bf16_t* __restrict__, const unsigned char* __restrict__, const float* __restrict__, \
       int, int, bf16_t* __restrict__, const MTile* __restrict__, const int32_t* __restrict__, \
-      const int32_t* __restrict__, int, int, int, int);
+      const int32_t* __restrict__, int, int, int, int, GuGrad);
+LCM_INST(2, false, false)
+LCM_INST(2, false, true)
 LCM_INST(0, false, false)
 LCM_INST(1, false, false)
 LCM_INST(0, true, false)
@@ -843,7 +866,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
 // few tokens, else the 320-row form (the M-tile list was built with the matching height).
 using PipeKernel = void (*)(const bf16_t*, const int32_t*, const bf16_t*, const bf16_t*,
                             const unsigned char*, const float*, int, int, bf16_t*, const MTile*,
-                            const int32_t*, const int32_t*, int, int, int, int);
+                            const int32_t*, const int32_t*, int, int, int, int, GuGrad);
 template <int MODE, bool FP8>
 PipeKernel pipe_kernel(const lc_moe_shape& s) {
   return ffn_small(s) ? ffn_bf16_pipe_kernel<MODE, FP8, true> : ffn_bf16_pipe_kernel<MODE, FP8, false>;
@@ -864,13 +887,13 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
       pipe_kernel<0, true>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, nullptr, nullptr, qb + q.codes_gu,
           reinterpret_cast<const float*>(qb + q.scales_gu), q.nrb_i, q.nrb_d,
-          static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
+          static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d, s.I, nn, 0, GuGrad{});
     else if (packed)
       pipe_kernel<0, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token,
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).gu),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf), mtiles, offsets, n_mtiles, s.d,
-          s.I, nn, 1);
+          s.I, nn, 1, GuGrad{});
     else if (ffn_small(s) && s.d % 64 == 0)
       ffn_bf16_line_kernel<0><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
@@ -880,7 +903,7 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
       pipe_kernel<0, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
           static_cast<const bf16_t*>(w_up), nullptr, nullptr, 0, 0, static_cast<bf16_t*>(hbuf),
-          mtiles, offsets, n_mtiles, s.d, s.I, nn, 0);
+          mtiles, offsets, n_mtiles, s.d, s.I, nn, 0, GuGrad{});
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.I + 127) / 128;
     const size_t units = size_t(mt_max) * nn;
@@ -901,6 +924,20 @@ hipError_t launch_ffn_gate_up(const lc_moe_shape& s, const void* x, const int32_
   return hipGetLastError();
 }
 
+hipError_t launch_ffn_gate_up_grad(const lc_moe_shape& s, const void* x, const int32_t* perm_token,
+                                   const void* w_gate, const void* w_up, const GuGrad& gg, void* gh,
+                                   const MTile* mtiles, const int32_t* offsets, const int32_t* n_mtiles,
+                                   int mt_max, hipStream_t st) {
+  const int nn = (s.I + 127) / 128;
+  const size_t units = size_t(mt_max) * nn;
+  const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8);
+  pipe_kernel<2, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
+      static_cast<const bf16_t*>(x), perm_token, static_cast<const bf16_t*>(w_gate),
+      static_cast<const bf16_t*>(w_up), nullptr, nullptr, 0, 0, static_cast<bf16_t*>(gh), mtiles, offsets,
+      n_mtiles, s.d, s.I, nn, 0, gg);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* w_down,
                            const void* fp8, const void* packed, void* ybuf, const MTile* mtiles,
                            const int32_t* offsets, const int32_t* n_mtiles, int mt_max,
@@ -915,13 +952,13 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
       pipe_kernel<1, true>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, nullptr, nullptr, qb + q.codes_d,
           reinterpret_cast<const float*>(qb + q.scales_d), q.nrb_d, q.nrb_i,
-          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn, 0);
+          static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d, nn, 0, GuGrad{});
     else if (packed)
       pipe_kernel<1, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr,
           reinterpret_cast<const bf16_t*>(static_cast<const unsigned char*>(packed) + plan_packed(s).d),
           nullptr, nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I,
-          s.d, nn, 1);
+          s.d, nn, 1, GuGrad{});
     else if (ffn_small(s) && s.I % 64 == 0)
       ffn_bf16_line_kernel<1><<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
@@ -930,7 +967,7 @@ hipError_t launch_ffn_down(const lc_moe_shape& s, const void* hbuf, const void* 
       pipe_kernel<1, false>(s)<<<dim3(grid), dim3(512), 0, st>>>(
           static_cast<const bf16_t*>(hbuf), nullptr, static_cast<const bf16_t*>(w_down), nullptr,
           nullptr, nullptr, 0, 0, static_cast<bf16_t*>(ybuf), mtiles, offsets, n_mtiles, s.I, s.d,
-          nn, 0);
+          nn, 0, GuGrad{});
   } else if (s.dtype == LC_MOE_BF16) {
     const int nn = (s.d + 255) / 256;
     const size_t units = size_t(mt_max) * nn;

@@ -436,4 +436,53 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s
   return hipGetLastError();
 }
 
+// M-tile list of height bm over the FFN experts' rows given by offsets [N+1]: expert e's
+// rows offsets[e] .. offsets[e+1]-1 in tiles of bm rows, experts in order (the list the scan
+// kernel builds at that height).  One 1024-thread workgroup; thread tid owns consecutive
+// experts, whose tile counts it scans with the others'.
+__global__ __launch_bounds__(1024) void mtile_list_kernel(const int32_t* __restrict__ offsets, int N, int bm,
+                                                          MTile* __restrict__ mtiles,
+                                                          int32_t* __restrict__ n_mtiles) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  int ms = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) ms += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  }
+  part[tid] = ms;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += a;
+    __syncthreads();
+  }
+  int m = tid > 0 ? part[tid - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < N) {
+      const int r0 = offsets[e], rows = offsets[e + 1] - r0;
+      const int nt = (rows + bm - 1) / bm;
+      for (int j = 0; j < nt; ++j) {
+        MTile mt;
+        mt.expert = e;
+        mt.row0 = r0 + j * bm;
+        mt.rows = min(bm, rows - j * bm);
+        mt.first_tile = m;
+        mtiles[m + j] = mt;
+      }
+      m += nt;
+    }
+  }
+  if (tid == 1023) *n_mtiles = part[1023];
+}
+
+hipError_t launch_mtile_list(const lc_moe_shape& s, const int32_t* offsets, int bm, MTile* mtiles,
+                             int32_t* n_mtiles, hipStream_t st) {
+  hipLaunchKernelGGL(mtile_list_kernel, dim3(1), dim3(1024), 0, st, offsets, s.N, bm, mtiles, n_mtiles);
+  return hipGetLastError();
+}
+
 }  // namespace lcm
