@@ -10,21 +10,22 @@
 //   gH_r   = g H_r;  dG_r = dH_r U (s + a (1 - s));  dU_r = dH_r a     (G and U recomputed by
 //            the forward's pipelined gate/up kernel with its backward epilogue, ffn.hip MODE 2)
 //   dX_r   = dG_r W_gate + dU_r W_up            (kind DX)
-//   dW_down_e = sum_r dy_r^T gH_r               (kind DWD)
-//   dW_gate_e = sum_r dG_r^T x_r, dW_up_e = sum_r dU_r^T x_r        (kind DWGU)
+//   dW_down_e = sum_r dy_r^T gH_r               (kind DWD, ffn_wgrad_kernel)
+//   dW_gate_e = sum_r dG_r^T x_r, dW_up_e = sum_r dU_r^T x_r        (kind DWGU, ffn_wgrad_kernel)
 //   dx_t = sum over the token's FFN picks, in pick order, of dX_r + (zero picks' gate sum) dy_t
 //
-// The other four products run on one grouped GEMM kernel, C[m][n] = sum_k A(m, k) B(n, k), bf16 on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Each operand is either K-contiguous
-// ("row": element (m, k) at row m, column k, as the forward's weights and activations) or
-// M-contiguous ("col": for a fixed k the m run contiguously, as W_down read along its
-// rows, or an activation matrix read along its tokens).  Both are staged in LDS as they lie
-// in memory (16-byte loads, 16-byte LDS writes); a row tile is read by the MFMA with one
-// 16-byte LDS read per fragment, a col tile with eight 2-byte reads.  So no operand needs
-// a transposed copy.  Tile 128 x 128, K step 32, 256 threads (2 x 2 waves of 64 x 64),
-// two LDS stages with the next step's loads in registers.  No atomics: every output
-// element is written once, by one workgroup, so the results are deterministic.
+// dH and dX run on one grouped GEMM kernel, C[m][n] = sum_k A(m, k) B(n, k), bf16 on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A is K-contiguous ("row": element (m, k)
+// at row m, column k: dy or dG/dU rows); B is N-contiguous ("col": for a fixed k the n run
+// contiguously: W_down read along its rows, W_gate and W_up along theirs).  Both are staged
+// in LDS as they lie in memory (16-byte loads, 16-byte LDS writes); a row tile is read by
+// the MFMA with one 16-byte LDS read per fragment, a col tile with two transposing reads.
+// So no weight needs a transposed copy.  Tile 128 x 128, K step 32, 256 threads (2 x 2
+// waves of 64 x 64), two LDS stages with the next step's loads in registers, four
+// workgroups per CU.  No atomics anywhere in the backward: every output element is written
+// once, by one workgroup, so the results are deterministic.
 #include "common.h"
+#include "lds_dma.h"
 
 namespace lcm {
 
@@ -59,57 +60,34 @@ struct BwArgs {
   bf16_t* dwg;
   bf16_t* dwu;
   bf16_t* dwd;
-  int n_ntiles;  // N-tiles per M-tile (activation kinds) or per expert and matrix (weight kinds)
-  int n_mt;      // weight kinds: M-tiles per matrix
-  int n_units;   // weight kinds: units in all
+  const bf16_t* xp;     // x rows gathered in FFN-row order [rows][d] (weight gradients)
+  const bf16_t* dyp;    // dy rows gathered the same way
+  const bf16_t* zero;   // 16 zero bytes (the source of operand chunks past the data)
+  int n_ntiles;  // N-tiles per M-tile (dH, dX)
 };
 
 template <int KIND>
 __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
   using namespace bw;
-  constexpr bool A_COL = KIND == DWD || KIND == DWGU;  // B is M-contiguous in every kind
+  static_assert(KIND == DH || KIND == DX, "activation kinds: A K-contiguous, B M-contiguous");
   __shared__ __attribute__((aligned(16))) bf16_t As[2][TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][TILE];
 
-  // ---- the work unit ------------------------------------------------------------------
-  int e, mrows, m0 = 0, n0, ktot, row0 = 0, mat = 0;
-  if constexpr (KIND == DH || KIND == DX) {
-    // (M-tile of an expert's rows, N-tile); XCD-aware order as in the forward
-    const int nmt = *a.n_mtiles, U = nmt * a.n_ntiles, per = (U + 7) >> 3;
-    const int slot = blockIdx.x >> 3;
-    if (slot >= per) return;
-    const int u = (blockIdx.x & 7) * per + slot;
-    if (u >= U) return;
-    const MTile tb = a.mtiles[u / a.n_ntiles];
-    const int mt = (a.offsets[tb.expert + 1] - a.offsets[tb.expert] + BM - 1) / BM;
-    const int ul = u - tb.first_tile * a.n_ntiles;
-    const int nt = ul / mt;
-    const MTile t = a.mtiles[tb.first_tile + (ul - nt * mt)];
-    e = t.expert;
-    row0 = t.row0;
-    mrows = t.rows;
-    n0 = nt * BN;
-    ktot = KIND == DX ? 2 * a.I : a.d;
-  } else {
-    // (expert, matrix, M-tile, N-tile), expert-major; K = the expert's rows
-    const int U = a.n_units, per = (U + 7) >> 3;
-    const int slot = blockIdx.x >> 3;
-    if (slot >= per) return;
-    const int u = (blockIdx.x & 7) * per + slot;
-    if (u >= U) return;
-    const int per_mat = a.n_mt * a.n_ntiles;
-    const int per_exp = per_mat * (KIND == DWGU ? 2 : 1);
-    e = u / per_exp;
-    int ul = u - e * per_exp;
-    mat = ul / per_mat;
-    ul -= mat * per_mat;
-    m0 = (ul / a.n_ntiles) * BM;
-    n0 = (ul % a.n_ntiles) * BN;
-    row0 = a.offsets[e];
-    ktot = a.offsets[e + 1] - row0;
-    mrows = (KIND == DWD ? a.d : a.I) - m0;
-  }
-  const int ncols = KIND == DH ? a.I : KIND == DX ? a.d : KIND == DWD ? a.I : a.d;
+  // ---- the work unit: (M-tile of an expert's rows, N-tile); XCD-aware order as in the forward
+  const int nmt = *a.n_mtiles, U = nmt * a.n_ntiles, per = (U + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int u = (blockIdx.x & 7) * per + slot;
+  if (u >= U) return;
+  const MTile tb = a.mtiles[u / a.n_ntiles];
+  const int mt = (a.offsets[tb.expert + 1] - a.offsets[tb.expert] + BM - 1) / BM;
+  const int ul = u - tb.first_tile * a.n_ntiles;
+  const int nt = ul / mt;
+  const MTile tile = a.mtiles[tb.first_tile + (ul - nt * mt)];
+  const int e = tile.expert, row0 = tile.row0, mrows = tile.rows;
+  const int n0 = nt * BN;
+  const int ktot = KIND == DX ? 2 * a.I : a.d;
+  const int ncols = KIND == DH ? a.I : a.d;
   const int tid = threadIdx.x;
 
   // ---- load assignment ----------------------------------------------------------------
@@ -118,54 +96,40 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
   const bf16_t* arow[2] = {nullptr, nullptr};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int q = tid + 256 * i;
-    if constexpr (!A_COL) {
-      const int r = q >> 2;
-      if (r < mrows) {
-        const size_t grow = size_t(row0 + r);
-        if (KIND == DH) arow[i] = a.dy + size_t(a.perm_token[grow]) * a.d;
-        else arow[i] = a.dg + grow * a.I;  // DX: dG for k < I, dU after (switched below)
-      }
+    const int r = (tid + 256 * i) >> 2;
+    if (r < mrows) {
+      const size_t grow = size_t(row0 + r);
+      if (KIND == DH) arow[i] = a.dy + size_t(a.perm_token[grow]) * a.d;
+      else arow[i] = a.dg + grow * a.I;  // DX: dG for k < I, dU after (switched below)
     }
   }
   uint4 ra[2], rb[2];
-  auto line_ptr = [&](int which, int k) -> const bf16_t* {
-    // which 0: A, 1: B; the start of line k (k < ktot) of a col operand, at column m0 / n0
+  // the start of line k (k < ktot) of the col operand B, at column n0
+  auto line_ptr = [&](int k) -> const bf16_t* {
     if constexpr (KIND == DH) {  // B: W_down[e] as [K = d][N = I]
       return a.wd + (size_t(e) * a.d + k) * a.I + n0;
-    } else if constexpr (KIND == DX) {  // B: W_gate[e] then W_up[e] as [K = I][N = d]
+    } else {  // DX, B: W_gate[e] then W_up[e] as [K = I][N = d]
       const bf16_t* w = k < a.I ? a.wg : a.wu;
       const int kk = k < a.I ? k : k - a.I;
       return w + (size_t(e) * a.I + kk) * a.d + n0;
-    } else if constexpr (KIND == DWD) {
-      if (which == 0) return a.dy + size_t(a.perm_token[row0 + k]) * a.d + m0;  // (m = j, k = r)
-      return a.gh + size_t(row0 + k) * a.I + n0;                                 // (n = i, k = r)
-    } else {  // DWGU
-      if (which == 0) return (mat == 0 ? a.dg : a.du) + size_t(row0 + k) * a.I + m0;  // (m = i, k = r)
-      return a.x + size_t(a.perm_token[row0 + k]) * a.d + n0;                         // (n = j, k = r)
     }
   };
-  const int mlim = KIND == DWD || KIND == DWGU ? mrows : 0;  // col A: valid m < mlim
-  const int nlim = ncols - n0;                                // col B: valid n < nlim
+  const int nlim = ncols - n0;  // valid n < nlim
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = tid + 256 * i;
-      // A
-      if constexpr (!A_COL) {
+      // A (row form)
+      {
         const int kc = (q & 3) * 8;
         const bf16_t* p = arow[i];
         if (KIND == DX && p && k0 >= a.I) p = a.du + (p - a.dg) - a.I;  // dU row, same offset
         ra[i] = p ? *reinterpret_cast<const uint4*>(p + k0 + kc) : make_uint4(0, 0, 0, 0);
-      } else {
-        const int k = k0 + (q >> 4), mc = (q & 15) * 8;
-        ra[i] = (k < ktot && mc < mlim) ? *reinterpret_cast<const uint4*>(line_ptr(0, k) + mc)
-                                        : make_uint4(0, 0, 0, 0);
       }
-      // B
+      // B (col form)
       {
         const int k = k0 + (q >> 4), nc = (q & 15) * 8;
-        rb[i] = (k < ktot && nc < nlim) ? *reinterpret_cast<const uint4*>(line_ptr(1, k) + nc)
+        rb[i] = (k < ktot && nc < nlim) ? *reinterpret_cast<const uint4*>(line_ptr(k) + nc)
                                         : make_uint4(0, 0, 0, 0);
       }
     }
@@ -174,8 +138,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = tid + 256 * i;
-      if constexpr (!A_COL) *reinterpret_cast<uint4*>(&As[buf][(q >> 2) * LDR + (q & 3) * 8]) = ra[i];
-      else *reinterpret_cast<uint4*>(&As[buf][(q >> 4) * LDC + (q & 15) * 8]) = ra[i];
+      *reinterpret_cast<uint4*>(&As[buf][(q >> 2) * LDR + (q & 3) * 8]) = ra[i];
       *reinterpret_cast<uint4*>(&Bs[buf][(q >> 4) * LDC + (q & 15) * 8]) = rb[i];
     }
   };
@@ -225,7 +188,7 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
       for (int ks = 0; ks < BK; ks += 16) {
         bf16x8 fa[2], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = frag(As[buf], A_COL, am[i], ks);
+        for (int i = 0; i < 2; ++i) fa[i] = frag(As[buf], false, am[i], ks);
 #pragma unroll
         for (int j = 0; j < 2; ++j) fb[j] = frag(Bs[buf], true, bn[j], ks);
 #pragma unroll
@@ -246,32 +209,257 @@ __global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int m = am[i] + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (m >= mrows) continue;
-      {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + bn[j] + lr;
-          if (col >= ncols) continue;
-          const float v = acc[i][j][r];
-          if constexpr (KIND == DH) {
-            a.dh[size_t(row0 + m) * a.I + col] = v * a.g_row[row0 + m];
-          } else if constexpr (KIND == DX) {
-            a.dxp[size_t(row0 + m) * a.d + col] = f2bf(v);
-          } else if constexpr (KIND == DWD) {
-            a.dwd[(size_t(e) * a.d + m0 + m) * a.I + col] = f2bf(v);
-          } else {
-            bf16_t* dw = mat == 0 ? a.dwg : a.dwu;
-            dw[(size_t(e) * a.I + m0 + m) * a.d + col] = f2bf(v);
-          }
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + bn[j] + lr;
+        if (col >= ncols) continue;
+        const float v = acc[i][j][r];
+        if constexpr (KIND == DH) a.dh[size_t(row0 + m) * a.I + col] = v * a.g_row[row0 + m];
+        else a.dxp[size_t(row0 + m) * a.d + col] = f2bf(v);
       }
     }
   }
 }
 
-// gate of each FFN row: g_row[slot_row[t][k]] = gate[t][k]
+// ---------------------------------------------------------------------------------------
+// Weight gradients on a persistent direct-load ring: dW_down_e = dY_e^T gH_e and
+// dW_gate_e, dW_up_e = dG_e^T X_e, dU_e^T X_e, the reductions running over the expert's rows.
+// Both operands lie with the reduction index slowest ([row][column]), so a stage of 32 rows
+// of each is staged as it lies (rows of 512 bytes = 256 columns of the tile) by direct
+// global->LDS loads and read with the transposing LDS read.  Tile 256 x 256 (64 MACs per
+// loaded byte), 512 threads = 8 waves of 64 rows x 128 columns, 4-stage ring of 32 KB
+// stages.  A unit (expert, matrix, 256-row block, 256-column block) has as many stages as
+// the expert has 32-row steps, often 8 to 10, so one workgroup per CU loops over its units
+// and the ring runs on across unit boundaries: the next unit's first stages load while
+// this one's last stages compute and its tile is stored.  Units of one expert run on one
+// XCD (each XCD takes a contiguous eighth of the unit order), where their shared rows meet
+// in its L2.  Rows past the expert's last and columns past the matrix load zeros.
+// LDS: 16-byte chunk c of a stage row r of either operand sits in the 32-byte granule
+// (c / 2) ^ 2 (r % 4); a transposing read's 16-lane groups then read the 4 rows of a group
+// from 8 distinct granules (64 banks).
+// ---------------------------------------------------------------------------------------
+namespace wg {
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int OPB = BK * BM * 2;   // bytes of one operand in one stage (16 KB)
+constexpr int STAGE = 2 * OPB;     // A then B (32 KB)
+constexpr int LDS = NST * STAGE;   // 128 KB
+constexpr int LOADS = 4;           // direct loads per wave and stage (2 per operand)
+}  // namespace wg
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void ffn_wgrad_kernel(BwArgs a) {
+  using namespace wg;
+  static_assert(KIND == bw::DWD || KIND == bw::DWGU, "weight-gradient kinds only");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
+  const int Mdim = KIND == bw::DWD ? a.d : a.I;  // rows of the gradient matrix
+  const int Ndim = KIND == bw::DWD ? a.I : a.d;  // its columns
+  const int n_mt = (Mdim + BM - 1) / BM, n_nt = (Ndim + BN - 1) / BN;
+  const int per_mat = n_mt * n_nt;
+  const int per_exp = (KIND == bw::DWGU ? 2 : 1) * per_mat;
+  const int U = a.N * per_exp;
+  // this workgroup's units: XCD x = blockIdx.x % 8 owns units [x U / 8, (x + 1) U / 8); its
+  // gridDim.x / 8 workgroups take every (gridDim.x / 8)-th of them
+  const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3, nsl = gridDim.x >> 3;
+  const int u_lo = int(int64_t(xcd) * U / 8), u_hi = int(int64_t(xcd + 1) * U / 8);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  struct Unit {
+    int e, mat, m0, n0, row0, ktot, nk;
+  };
+  auto decode = [&](int u) {
+    Unit t;
+    t.e = __builtin_amdgcn_readfirstlane(u / per_exp);
+    int r = u - t.e * per_exp;
+    t.mat = r / per_mat;
+    r -= t.mat * per_mat;
+    t.m0 = (r / n_nt) * BM;
+    t.n0 = (r % n_nt) * BN;
+    // offsets[e], offsets[e+1] through one scalar load (waited for in the same block): a
+    // vector load here would make the compiler wait for every direct load in flight, which
+    // empties the ring at each unit boundary
+    uint64_t oo;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=s"(oo)
+                 : "s"(a.offsets + t.e)
+                 : "memory");
+    t.row0 = int(uint32_t(oo));
+    t.ktot = int(uint32_t(oo >> 32)) - t.row0;
+    t.nk = (t.ktot + BK - 1) / BK;
+    return t;
+  };
+
+  // ---- the load stream: stage (unit, kt) of this workgroup's units with rows --------------
+  // Wave w's load i (i < 2) of an operand fills stage rows 2 (w + 8 i) and 2 (w + 8 i) + 1:
+  // lane l writes row 2 (w + 8 i) + l / 32, 16-byte slot l % 32, with logical chunk
+  // 2 ((slot / 2) ^ 2 (row % 4)) + slot % 2 of that row.
+  int iu = u_lo + sl, ikt = 0, issued = 0;
+  Unit iunit{};
+  auto iskip = [&]() {
+    for (; iu < u_hi; iu += nsl) {
+      iunit = decode(iu);
+      if (iunit.nk > 0) break;
+    }
+  };
+  iskip();
+  const int slot16 = lane & 31;
+  auto issue = [&](int slot) {
+    unsigned char* st = smem + slot * STAGE;
+    const Unit& t = iunit;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int kr = 2 * (wave + 8 * i) + (lane >> 5);                       // stage row
+      const int c = 2 * ((slot16 >> 1) ^ (2 * (kr & 3))) + (slot16 & 1);      // logical chunk
+      const int k = ikt * BK + kr;                                          // expert row
+      const size_t row = size_t(t.row0 + k);
+      const bool kin = k < t.ktot;
+      // A: (m, k) = the row's column m0 + m
+      const int ma = t.m0 + c * 8;
+      const bf16_t* srca;
+      if constexpr (KIND == bw::DWD) srca = a.dyp + row * a.d + ma;
+      else srca = (t.mat == 0 ? a.dg : a.du) + row * a.I + ma;
+      dma16(kin && ma < Mdim ? srca : a.zero, st + (wave + 8 * i) * 1024);
+      // B: (n, k) = the row's column n0 + n
+      const int nb = t.n0 + c * 8;
+      const bf16_t* srcb;
+      if constexpr (KIND == bw::DWD) srcb = a.gh + row * a.I + nb;
+      else srcb = a.xp + row * a.d + nb;
+      dma16(kin && nb < Ndim ? srcb : a.zero, st + OPB + (wave + 8 * i) * 1024);
+    }
+    ++issued;
+    if (++ikt == t.nk) {
+      ikt = 0;
+      iu += nsl;
+      iskip();
+    }
+  };
+
+  // ---- fragments: transposing reads (see ffn_backward_kernel) with the granule swizzle ----
+  // A substep's 12 reads (2 per fragment: k rows +0..3 and +4..7) go out in one asm block
+  // that waits for them itself.  Written with the builtin, each read got a wait for every
+  // direct load in flight (the compiler cannot tell the stage it reads from the stages
+  // still loading), which emptied the ring at every step; the explicit vmcnt waits and
+  // the barrier already order the reads after their stage's loads.
+  const int tr_j = (lane >> 2) & 3;                  // the row in its group of 4 (= row % 4)
+  const int tr_row = 8 * (lane >> 5) + tr_j;         // + 4 h + substep
+  const int tr_g = (lane >> 4) & 1;                  // + column granule base / 16
+  const int tr_byte = 8 * (lane & 3);
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  auto lds_addr = [&](const unsigned char* op, int base, int ks) -> uint32_t {
+    const int lg = (base >> 4) + tr_g;
+    const unsigned char* p = op + (ks + tr_row) * 512 + ((lg ^ (2 * tr_j)) << 5) + tr_byte;
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(reinterpret_cast<const lds_u8*>(
+        reinterpret_cast<uintptr_t>(p))));
+  };
+  auto frags = [&](const unsigned char* st, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
+    const uint32_t a0 = lds_addr(st, wm * 64, ks), a1 = lds_addr(st, wm * 64 + 32, ks);
+    const uint32_t b0 = lds_addr(st + OPB, wn * 128, ks), b1 = lds_addr(st + OPB, wn * 128 + 32, ks);
+    const uint32_t b2 = lds_addr(st + OPB, wn * 128 + 64, ks), b3 = lds_addr(st + OPB, wn * 128 + 96, ks);
+    uint64_t r[12];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %12\n"
+        "ds_read_b64_tr_b16 %1, %12 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %13\n"
+        "ds_read_b64_tr_b16 %3, %13 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %14\n"
+        "ds_read_b64_tr_b16 %5, %14 offset:2048\n"
+        "ds_read_b64_tr_b16 %6, %15\n"
+        "ds_read_b64_tr_b16 %7, %15 offset:2048\n"
+        "ds_read_b64_tr_b16 %8, %16\n"
+        "ds_read_b64_tr_b16 %9, %16 offset:2048\n"
+        "ds_read_b64_tr_b16 %10, %17\n"
+        "ds_read_b64_tr_b16 %11, %17 offset:2048\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+        : "memory");
+    auto pack = [](uint64_t lo, uint64_t hi) {
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+      return __builtin_bit_cast(bf16x8, u64x2{lo, hi});
+    };
+    fa[0] = pack(r[0], r[1]);
+    fa[1] = pack(r[2], r[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = pack(r[4 + 2 * j], r[5 + 2 * j]);
+  };
+
+  f32x16 acc[2][4];
+  for (int s = 0; s < NST - 1 && iu < u_hi; ++s) issue(s);
+  int g = 0;  // stages consumed
+  for (int cu = u_lo + sl; cu < u_hi; cu += nsl) {
+    const Unit t = decode(cu);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kt = 0; kt < t.nk; ++kt, ++g) {
+      wait_vmcnt((issued - 1 - g) * LOADS);  // this wave's loads of stage g landed
+      wait_lds_reads();
+      block_barrier();  // every wave's loads of stage g visible; stage g-1 read by all
+      if (iu < u_hi) issue(issued % NST);  // stage g+NST-1 into stage g-1's slot
+      const unsigned char* st = smem + (g % NST) * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < BK; ks += 16) {
+        bf16x8 fa[2], fb[4];
+        frags(st, ks, fa, fb);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    // ---- the unit's tile (zeros for an expert without rows).  32x32 D layout: column
+    // lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.  Lanes 4q .. 4q+3 hold a 4 x 4
+    // block (4 rows r % 4 = 0..3 of columns 4q .. 4q+3); a transpose among them gives each
+    // lane one row of 4 columns, stored as 8 bytes.
+    bf16_t* out;
+    if constexpr (KIND == bw::DWD) out = a.dwd + (size_t(t.e) * a.d + t.m0) * a.I + t.n0;
+    else out = (t.mat == 0 ? a.dwg : a.dwu) + (size_t(t.e) * a.I + t.m0) * a.d + t.n0;
+    const int q4 = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float v[4];
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4) v[t4] = acc[i][j][rq * 4 + t4];
+          // lane q4 keeps row q4: its own v[q4] is column q4; column q4 ^ s comes from
+          // lane q4 ^ s, which sends its v[q4] (row q4 of its column)
+          float w[4];
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            float send = v[0];
+#pragma unroll
+            for (int t4 = 1; t4 < 4; ++t4) send = (q4 ^ s4) == t4 ? v[t4] : send;
+            const float got = s4 == 0 ? send : __shfl_xor(send, s4);
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) w[c4] = c4 == (q4 ^ s4) ? got : (s4 == 0 ? 0.f : w[c4]);
+          }
+          const int m = wm * 64 + i * 32 + 8 * rq + 4 * (lane >> 5) + q4;
+          const int n = wn * 128 + j * 32 + (lane & 28);
+          if (m < Mdim - t.m0 && n < Ndim - t.n0) {
+            const uint32_t lo = f2bf(w[0]) | (uint32_t(f2bf(w[1])) << 16);
+            const uint32_t hi = f2bf(w[2]) | (uint32_t(f2bf(w[3])) << 16);
+            *reinterpret_cast<uint2*>(out + size_t(m) * Ndim + n) = make_uint2(lo, hi);
+          }
+        }
+  }
+}
+
+// gate of each FFN row: g_row[slot_row[t][k]] = gate[t][k]; and the 16 zero bytes
 __global__ __launch_bounds__(256) void row_gates_kernel(const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ gate,
-                                                        float* __restrict__ g_row, size_t tk) {
+                                                        float* __restrict__ g_row, size_t tk,
+                                                        uint4* __restrict__ zero) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *zero = make_uint4(0, 0, 0, 0);
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < tk; i += size_t(gridDim.x) * 256) {
     const int r = slot_row[i];
     if (r >= 0) g_row[r] = gate[i];
@@ -347,11 +535,14 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
   a.dwg = static_cast<bf16_t*>(dw_gate);
   a.dwu = static_cast<bf16_t*>(dw_up);
   a.dwd = static_cast<bf16_t*>(dw_down);
+  a.xp = reinterpret_cast<const bf16_t*>(w + p.xp);
+  a.dyp = reinterpret_cast<const bf16_t*>(w + p.dyp);
+  a.zero = reinterpret_cast<const bf16_t*>(w + p.zero);
 
   const size_t tk = size_t(s.T) * s.K;
   hipLaunchKernelGGL(row_gates_kernel, dim3(unsigned(tk / 256 + 1 < 4096 ? tk / 256 + 1 : 4096)), dim3(256), 0,
                      st, reinterpret_cast<const int32_t*>(w + p.slot_row), gate, reinterpret_cast<float*>(w + p.g_row),
-                     tk);
+                     tk, reinterpret_cast<uint4*>(w + p.zero));
   auto grid_of = [](size_t units) { return dim3(unsigned((units + 7) / 8 * 8)); };
   // activation kinds: units over the M-tile list
   a.n_ntiles = (s.I + BN - 1) / BN;
@@ -366,15 +557,19 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
   if (err != hipSuccess) return err;
   a.n_ntiles = (s.d + BN - 1) / BN;
   hipLaunchKernelGGL(ffn_backward_kernel<DX>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
-  // weight kinds: every expert (an expert without rows gets zero gradients)
-  a.n_mt = (s.d + BM - 1) / BM;
-  a.n_ntiles = (s.I + BN - 1) / BN;
-  a.n_units = s.N * a.n_mt * a.n_ntiles;
-  hipLaunchKernelGGL(ffn_backward_kernel<DWD>, grid_of(size_t(a.n_units)), dim3(256), 0, st, a);
-  a.n_mt = (s.I + BM - 1) / BM;
-  a.n_ntiles = (s.d + BN - 1) / BN;
-  a.n_units = s.N * 2 * a.n_mt * a.n_ntiles;
-  hipLaunchKernelGGL(ffn_backward_kernel<DWGU>, grid_of(size_t(a.n_units)), dim3(256), 0, st, a);
+  // weight kinds: every expert (an expert without rows gets zero gradients), one persistent
+  // workgroup per CU over the gathered x and dy rows
+  err = launch_gather_rows(s, x, a.perm_token, a.offsets, w + p.xp, st);
+  if (err != hipSuccess) return err;
+  err = launch_gather_rows(s, dy, a.perm_token, a.offsets, w + p.dyp, st);
+  if (err != hipSuccess) return err;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const dim3 pgrid(unsigned(cus >= 8 ? cus / 8 * 8 : 8));
+  hipLaunchKernelGGL(ffn_wgrad_kernel<DWD>, pgrid, dim3(512), 0, st, a);
+  hipLaunchKernelGGL(ffn_wgrad_kernel<DWGU>, pgrid, dim3(512), 0, st, a);
   hipLaunchKernelGGL(dx_combine_kernel, dim3(s.T), dim3(256), 0, st, a.dxp, a.dy,
                      reinterpret_cast<const int32_t*>(w + p.slot_row), gate, static_cast<bf16_t*>(dx), s.d, s.K);
   return hipGetLastError();

@@ -195,7 +195,7 @@ inline bool grids_fit(const lc_moe_shape& s) {
 constexpr int kBmBwd = 128;
 struct BwPlan {
   size_t block_counts, block_base, load, offsets, mtiles, n_mtiles, done, perm_token, slot_row, g_row,
-      dh, gh, dg, du, dxp, pipe_mtiles, pipe_n_mtiles, total;
+      dh, gh, dg, du, dxp, pipe_mtiles, pipe_n_mtiles, xp, dyp, zero, total;
   int nblocks, mt_max;
   int pipe_bm, pipe_mt_max;  // the M-tile list of the pipelined gate/up kernel's recompute
 };
@@ -230,6 +230,10 @@ inline BwPlan plan_backward(const lc_moe_shape& s) {
   p.pipe_mt_max = int(mt2);
   p.pipe_mtiles = take(mt2 * sizeof(MTile));
   p.pipe_n_mtiles = take(4);
+  // x and dy rows gathered in FFN-row order, and 16 zero bytes, for the weight gradients
+  p.xp = take(tk * size_t(s.d) * 2);
+  p.dyp = take(tk * size_t(s.d) * 2);
+  p.zero = take(16);
   p.total = o;
   return p;
 }
