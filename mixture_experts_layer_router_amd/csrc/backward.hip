@@ -14,29 +14,19 @@
 //   dW_gate_e = sum_r dG_r^T x_r, dW_up_e = sum_r dU_r^T x_r        (kind DWGU, ffn_wgrad_kernel)
 //   dx_t = sum over the token's FFN picks, in pick order, of dX_r + (zero picks' gate sum) dy_t
 //
-// dH and dX run on one grouped GEMM kernel, C[m][n] = sum_k A(m, k) B(n, k), bf16 on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A is K-contiguous ("row": element (m, k)
-// at row m, column k: dy or dG/dU rows); B is N-contiguous ("col": for a fixed k the n run
-// contiguously: W_down read along its rows, W_gate and W_up along theirs).  Both are staged
-// in LDS as they lie in memory (16-byte loads, 16-byte LDS writes); a row tile is read by
-// the MFMA with one 16-byte LDS read per fragment, a col tile with two transposing reads.
-// So no weight needs a transposed copy.  Tile 128 x 128, K step 32, 256 threads (2 x 2
-// waves of 64 x 64), two LDS stages with the next step's loads in registers, four
-// workgroups per CU.  No atomics anywhere in the backward: every output element is written
-// once, by one workgroup, so the results are deterministic.
+// Every product is a bf16 grouped GEMM on v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+// its operands staged in LDS as they lie in memory by direct global->LDS loads: an operand
+// whose reduction index is contiguous (dy, dG, dU rows) as the forward stages its rows, one
+// whose output index is contiguous (W_down, W_gate, W_up read along their rows; activation
+// rows read along the tokens) in 512-byte rows read by gfx950's transposing LDS read.  So no
+// weight or activation needs a transposed copy.  No atomics: every output element is
+// written once, by one workgroup, so the results are deterministic.
 #include "common.h"
 #include "lds_dma.h"
 
 namespace lcm {
 
 namespace bw {
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDR = BK + 8;    // row tile: [128][40] bf16 (80-byte rows)
-// col tile: [32][160] bf16 (320-byte rows: a transposing read's four 16-lane groups read
-// rows 16 dwords apart, 32 bytes each, on 64 distinct banks)
-constexpr int LDC = BM + 32;
-constexpr int TILE = BM * LDR; // elements per operand and stage (both forms: 128 x 40 = 32 x 160)
-static_assert(BK * LDC <= TILE, "col tile must fit the stage");
 enum { DH = 0, DX = 2, DWD = 3, DWGU = 4 };  // (1: G/U, on the pipelined gate/up kernel)
 }  // namespace bw
 
@@ -50,8 +40,6 @@ struct BwArgs {
   const int32_t* perm_token;
   const float* g_row;
   const int32_t* offsets;
-  const MTile* mtiles;
-  const int32_t* n_mtiles;
   float* dh;
   bf16_t* gh;
   bf16_t* dg;
@@ -65,161 +53,6 @@ struct BwArgs {
   const bf16_t* zero;   // 16 zero bytes (the source of operand chunks past the data)
   int n_ntiles;  // N-tiles per M-tile (dH, dX)
 };
-
-template <int KIND>
-__global__ __launch_bounds__(256, 4) void ffn_backward_kernel(BwArgs a) {
-  using namespace bw;
-  static_assert(KIND == DH || KIND == DX, "activation kinds: A K-contiguous, B M-contiguous");
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][TILE];
-
-  // ---- the work unit: (M-tile of an expert's rows, N-tile); XCD-aware order as in the forward
-  const int nmt = *a.n_mtiles, U = nmt * a.n_ntiles, per = (U + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int u = (blockIdx.x & 7) * per + slot;
-  if (u >= U) return;
-  const MTile tb = a.mtiles[u / a.n_ntiles];
-  const int mt = (a.offsets[tb.expert + 1] - a.offsets[tb.expert] + BM - 1) / BM;
-  const int ul = u - tb.first_tile * a.n_ntiles;
-  const int nt = ul / mt;
-  const MTile tile = a.mtiles[tb.first_tile + (ul - nt * mt)];
-  const int e = tile.expert, row0 = tile.row0, mrows = tile.rows;
-  const int n0 = nt * BN;
-  const int ktot = KIND == DX ? 2 * a.I : a.d;
-  const int ncols = KIND == DH ? a.I : a.d;
-  const int tid = threadIdx.x;
-
-  // ---- load assignment ----------------------------------------------------------------
-  // row tile: chunk q = tid + 256 i (i < 2): row q / 4, k offset (q % 4) * 8
-  // col tile: chunk q: line k = q / 16, m offset (q % 16) * 8
-  const bf16_t* arow[2] = {nullptr, nullptr};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid + 256 * i) >> 2;
-    if (r < mrows) {
-      const size_t grow = size_t(row0 + r);
-      if (KIND == DH) arow[i] = a.dy + size_t(a.perm_token[grow]) * a.d;
-      else arow[i] = a.dg + grow * a.I;  // DX: dG for k < I, dU after (switched below)
-    }
-  }
-  uint4 ra[2], rb[2];
-  // the start of line k (k < ktot) of the col operand B, at column n0
-  auto line_ptr = [&](int k) -> const bf16_t* {
-    if constexpr (KIND == DH) {  // B: W_down[e] as [K = d][N = I]
-      return a.wd + (size_t(e) * a.d + k) * a.I + n0;
-    } else {  // DX, B: W_gate[e] then W_up[e] as [K = I][N = d]
-      const bf16_t* w = k < a.I ? a.wg : a.wu;
-      const int kk = k < a.I ? k : k - a.I;
-      return w + (size_t(e) * a.I + kk) * a.d + n0;
-    }
-  };
-  const int nlim = ncols - n0;  // valid n < nlim
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
-      // A (row form)
-      {
-        const int kc = (q & 3) * 8;
-        const bf16_t* p = arow[i];
-        if (KIND == DX && p && k0 >= a.I) p = a.du + (p - a.dg) - a.I;  // dU row, same offset
-        ra[i] = p ? *reinterpret_cast<const uint4*>(p + k0 + kc) : make_uint4(0, 0, 0, 0);
-      }
-      // B (col form)
-      {
-        const int k = k0 + (q >> 4), nc = (q & 15) * 8;
-        rb[i] = (k < ktot && nc < nlim) ? *reinterpret_cast<const uint4*>(line_ptr(k) + nc)
-                                        : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&As[buf][(q >> 2) * LDR + (q & 3) * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][(q >> 4) * LDC + (q & 15) * 8]) = rb[i];
-    }
-  };
-
-  // ---- MFMA -----------------------------------------------------------------------------
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  // tile rows of the wave's two A blocks and two B blocks
-  const int am[2] = {wm * 64, wm * 64 + 32};
-  const int bn[2] = {wn * 64, wn * 64 + 32};
-  // fragment of one 32-row block at k offset kk: 8 consecutive k of row (base + lane % 32).
-  // A col tile holds [k][m]; gfx950's transposing LDS read (ds_read_b64_tr_b16) gives lane
-  // 16g + 4a + b element b of the 8 bytes addressed by lanes 16g + 4j + a, j = 0..3, as its
-  // element j.  So lane 16g + 4j + a points at k row kk + 8 (g / 2) + 4 h + j, m column
-  // base + 16 (g % 2) + 4 a: two reads (h = 0, 1) give the lane's 8 k values of row
-  // base + lane % 32.
-  const int tr_k = 8 * (lane >> 5) + ((lane >> 2) & 3), tr_m = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto frag = [&](const bf16_t* tile, bool colform, int base, int kk) -> bf16x8 {
-    if (!colform) return *reinterpret_cast<const bf16x8*>(tile + (base + lr) * LDR + kk + lk);
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const bf16_t* p = tile + (kk + tr_k) * LDC + base + tr_m;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * LDC));
-    return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                                hi[0], hi[1], hi[2], hi[3]});
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = (ktot + BK - 1) / BK;
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * BK);
-#pragma unroll
-      for (int ks = 0; ks < BK; ks += 16) {
-        bf16x8 fa[2], fb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = frag(As[buf], false, am[i], ks);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = frag(Bs[buf], true, bn[j], ks);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) store(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue; 32x32 D layout: column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4 --
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = am[i] + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m >= mrows) continue;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + bn[j] + lr;
-        if (col >= ncols) continue;
-        const float v = acc[i][j][r];
-        if constexpr (KIND == DH) a.dh[size_t(row0 + m) * a.I + col] = v * a.g_row[row0 + m];
-        else a.dxp[size_t(row0 + m) * a.d + col] = f2bf(v);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------------------
 // Weight gradients on a persistent direct-load ring: dW_down_e = dY_e^T gH_e and
@@ -454,6 +287,209 @@ __global__ __launch_bounds__(512, 1) void ffn_wgrad_kernel(BwArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// dH = g dY W_down and dX = dG W_gate + dU W_up on a direct-load ring: work unit (256-row
+// M-tile of an expert's rows, 256 output columns), K = d (dH) or 2 I (dX: dG against W_gate,
+// then dU against W_up).  A (dY rows gathered in FFN-row order, or dG / dU rows) is
+// K-contiguous: staged as the forward stages its activation rows (64-byte LDS rows, 16-byte
+// chunk c of row r in slot c ^ swz4(r)) and read with 16-byte reads.  B (W_down, W_gate,
+// W_up rows) is N-contiguous: staged as the weight-gradient kernel stages its operands
+// (512-byte rows, 32-byte-granule swizzle) and read with transposing reads.  512 threads =
+// 8 waves of 64 rows x 128 columns, 4-stage ring of 32 KB stages, one workgroup per CU,
+// XCD-aware unit order as in the forward.  Rows past the tile read the tile's first row
+// (never stored); columns past the matrix load zeros.
+// ---------------------------------------------------------------------------------------
+namespace ba {
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int A_BYTES = BM * 64;       // 16 KB
+constexpr int B_BYTES = BK * BN * 2;   // 16 KB
+constexpr int STAGE = A_BYTES + B_BYTES, LDS = NST * STAGE;  // 128 KB
+constexpr int LOADS = 4;               // direct loads per wave and stage
+}  // namespace ba
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void ffn_bwd_act_kernel(BwArgs a, const MTile* __restrict__ mtiles,
+                                                             const int32_t* __restrict__ n_mtiles_ptr) {
+  using namespace ba;
+  static_assert(KIND == bw::DH || KIND == bw::DX, "activation kinds");
+  static_assert(BM == kBmBwd, "the M-tile list is the backward permutation's");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
+  const int ncols = KIND == bw::DH ? a.I : a.d;
+  const int n_nt = a.n_ntiles;
+  // (M-tile, n-tile) unit, XCD-aware as in the forward
+  const int U = *n_mtiles_ptr * n_nt, per = (U + 7) >> 3;
+  const int slot_w = blockIdx.x >> 3;
+  if (slot_w >= per) return;
+  const int u = (blockIdx.x & 7) * per + slot_w;
+  if (u >= U) return;
+  const MTile tb = mtiles[u / n_nt];
+  const int mt = (a.offsets[tb.expert + 1] - a.offsets[tb.expert] + BM - 1) / BM;
+  const int ul = u - tb.first_tile * n_nt;
+  const int ntile = ul / mt;
+  const MTile tile = mtiles[tb.first_tile + (ul - ntile * mt)];
+  const int e = tile.expert, row0 = tile.row0, rows = tile.rows;
+  const int n0 = ntile * BN;
+  const int nk = (KIND == bw::DX ? 2 * a.I : a.d) / BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- loads: wave w's A loads q = w, w + 8 fill rows 16 q .. 16 q + 15 (lane l: row
+  // 16 q + l / 4, slot l % 4, global chunk (l % 4) ^ swz4(row)); its B loads q = w, w + 8
+  // fill k rows 2 q, 2 q + 1 (lane l: row 2 q + l / 32, 16-byte slot l % 32 with logical
+  // chunk 2 ((slot / 2) ^ 2 (row % 4)) + slot % 2)
+  size_t arow_off[2];
+  int acol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave + 8 * i) * 16 + (lane >> 2);
+    arow_off[i] = size_t(row0 + (r < rows ? r : 0));
+    acol[i] = ((lane & 3) ^ swz4(r)) * 8;
+  }
+  const int slot16 = lane & 31;
+  auto issue = [&](int kt, int slot) {
+    unsigned char* st = smem + slot * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16_t* srca;
+      if constexpr (KIND == bw::DH) srca = a.dyp + arow_off[i] * a.d + k0 + acol[i];
+      else srca = (k0 < a.I ? a.dg + arow_off[i] * a.I + k0 : a.du + arow_off[i] * a.I + (k0 - a.I)) + acol[i];
+      dma16(srca, st + (wave + 8 * i) * 1024);
+      const int kr = 2 * (wave + 8 * i) + (lane >> 5);
+      const int c = 2 * ((slot16 >> 1) ^ (2 * (kr & 3))) + (slot16 & 1);
+      const int n = n0 + c * 8;
+      const int k = k0 + kr;
+      const bf16_t* srcb;
+      if constexpr (KIND == bw::DH) srcb = a.wd + (size_t(e) * a.d + k) * a.I + n;  // W_down[e] as [d][I]
+      else srcb = (k < a.I ? a.wg + (size_t(e) * a.I + k) * a.d : a.wu + (size_t(e) * a.I + (k - a.I)) * a.d) + n;
+      dma16(n < ncols ? srcb : a.zero, st + A_BYTES + (wave + 8 * i) * 1024);
+    }
+  };
+
+  // ---- fragments -------------------------------------------------------------------------
+  const int l32 = lane & 31, khalf = lane >> 5, sw = swz4(l32);
+  const int tr_j = (lane >> 2) & 3, tr_row = 8 * (lane >> 5) + tr_j, tr_g = (lane >> 4) & 1;
+  const int tr_byte = 8 * (lane & 3);
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  auto lds_addr = [&](const unsigned char* p) -> uint32_t {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(reinterpret_cast<const lds_u8*>(
+        reinterpret_cast<uintptr_t>(p))));
+  };
+  auto b_addr = [&](const unsigned char* bop, int base, int ks) -> uint32_t {
+    const int lg = (base >> 4) + tr_g;
+    return lds_addr(bop + (ks + tr_row) * 512 + ((lg ^ (2 * tr_j)) << 5) + tr_byte);
+  };
+  auto frags = [&](const unsigned char* st, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
+    const int c = ks / 8 + khalf;  // the lane's 16-byte chunk of the A rows
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(st + (wm * 64 + i * 32 + l32) * 64 + ((c ^ sw) << 4));
+    const unsigned char* bop = st + A_BYTES;
+    const uint32_t b0 = b_addr(bop, wn * 128, ks), b1 = b_addr(bop, wn * 128 + 32, ks);
+    const uint32_t b2 = b_addr(bop, wn * 128 + 64, ks), b3 = b_addr(bop, wn * 128 + 96, ks);
+    uint64_t r[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %9\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %10\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:2048\n"
+        "ds_read_b64_tr_b16 %6, %11\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:2048\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+        : "memory");
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8, u64x2{r[2 * j], r[2 * j + 1]});
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int npro = nk < NST - 1 ? nk : NST - 1;
+  for (int s2 = 0; s2 < npro; ++s2) issue(s2, s2);
+  int issued = npro;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt((issued - 1 - kt) * LOADS);  // this wave's loads of stage kt landed
+    wait_lds_reads();
+    block_barrier();  // every wave's loads of stage kt visible; stage kt-1 read by all
+    if (issued < nk) {
+      issue(issued, issued % NST);  // stage kt+NST-1 into stage kt-1's slot
+      ++issued;
+    }
+    const unsigned char* st = smem + (kt % NST) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8 fa[2], fb[4];
+      frags(st, ks, fa, fb);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: 4-lane transposes (see ffn_wgrad_kernel), one row of 4 columns per lane --
+  const int q4 = lane & 3;
+  // dH: the gates of the lane's 8 rows, loaded before the first store (a load between the
+  // stores would wait for every store before it)
+  float grow[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int m = wm * 64 + i * 32 + 8 * rq + 4 * (lane >> 5) + q4;
+      grow[i][rq] = KIND == bw::DH && m < rows ? a.g_row[row0 + m] : 0.f;
+    }
+  // the loads complete here, not next to their first use among the stores
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) asm volatile("" : "+v"(grow[i][rq]));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float v[4], w[4];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) v[t4] = acc[i][j][rq * 4 + t4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          float send = v[0];
+#pragma unroll
+          for (int t4 = 1; t4 < 4; ++t4) send = (q4 ^ s4) == t4 ? v[t4] : send;
+          const float got = s4 == 0 ? send : __shfl_xor(send, s4);
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) w[c4] = c4 == (q4 ^ s4) ? got : (s4 == 0 ? 0.f : w[c4]);
+        }
+        const int m = wm * 64 + i * 32 + 8 * rq + 4 * (lane >> 5) + q4;
+        const int n = n0 + wn * 128 + j * 32 + (lane & 28);
+        if (m < rows && n < ncols) {
+          const size_t r = size_t(row0 + m);
+          if constexpr (KIND == bw::DH) {
+            const float g = grow[i][rq];
+            *reinterpret_cast<float4*>(a.dh + r * a.I + n) = make_float4(w[0] * g, w[1] * g, w[2] * g, w[3] * g);
+          } else {
+            const uint32_t lo = f2bf(w[0]) | (uint32_t(f2bf(w[1])) << 16);
+            const uint32_t hi = f2bf(w[2]) | (uint32_t(f2bf(w[3])) << 16);
+            *reinterpret_cast<uint2*>(a.dxp + r * a.d + n) = make_uint2(lo, hi);
+          }
+        }
+      }
+}
+
 // gate of each FFN row: g_row[slot_row[t][k]] = gate[t][k]; and the 16 zero bytes
 __global__ __launch_bounds__(256) void row_gates_kernel(const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ gate,
@@ -525,8 +561,6 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
   a.perm_token = reinterpret_cast<const int32_t*>(w + p.perm_token);
   a.g_row = reinterpret_cast<const float*>(w + p.g_row);
   a.offsets = reinterpret_cast<const int32_t*>(w + p.offsets);
-  a.mtiles = reinterpret_cast<const MTile*>(w + p.mtiles);
-  a.n_mtiles = reinterpret_cast<const int32_t*>(w + p.n_mtiles);
   a.dh = reinterpret_cast<float*>(w + p.dh);
   a.gh = reinterpret_cast<bf16_t*>(w + p.gh);
   a.dg = reinterpret_cast<bf16_t*>(w + p.dg);
@@ -544,25 +578,33 @@ hipError_t launch_ffn_backward(const lc_moe_shape& s, const BwPlan& p, void* ws,
                      st, reinterpret_cast<const int32_t*>(w + p.slot_row), gate, reinterpret_cast<float*>(w + p.g_row),
                      tk, reinterpret_cast<uint4*>(w + p.zero));
   auto grid_of = [](size_t units) { return dim3(unsigned((units + 7) / 8 * 8)); };
-  // activation kinds: units over the M-tile list
-  a.n_ntiles = (s.I + BN - 1) / BN;
-  hipLaunchKernelGGL(ffn_backward_kernel<DH>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
-  // G and U recomputed on the forward's pipelined gate/up kernel (its own M-tile height)
-  MTile* pipe_mtiles = reinterpret_cast<MTile*>(w + p.pipe_mtiles);
-  int32_t* pipe_n = reinterpret_cast<int32_t*>(w + p.pipe_n_mtiles);
-  hipError_t err = launch_mtile_list(s, a.offsets, p.pipe_bm, pipe_mtiles, pipe_n, st);
-  if (err != hipSuccess) return err;
-  err = launch_ffn_gate_up_grad(s, x, a.perm_token, w_gate, w_up, GuGrad{a.dh, a.g_row, a.dg, a.du}, a.gh,
-                                pipe_mtiles, a.offsets, pipe_n, p.pipe_mt_max, st);
-  if (err != hipSuccess) return err;
-  a.n_ntiles = (s.d + BN - 1) / BN;
-  hipLaunchKernelGGL(ffn_backward_kernel<DX>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(256), 0, st, a);
-  // weight kinds: every expert (an expert without rows gets zero gradients), one persistent
-  // workgroup per CU over the gathered x and dy rows
-  err = launch_gather_rows(s, x, a.perm_token, a.offsets, w + p.xp, st);
+  // x and dy rows in FFN-row order (dH, dW_down and dW_gate / dW_up read them contiguously)
+  hipError_t err = launch_gather_rows(s, x, a.perm_token, a.offsets, w + p.xp, st);
   if (err != hipSuccess) return err;
   err = launch_gather_rows(s, dy, a.perm_token, a.offsets, w + p.dyp, st);
   if (err != hipSuccess) return err;
+  // the M-tile lists: the permutation's (256 rows) for dH and dX, one at the pipelined
+  // gate/up kernel's height for G, U
+  const MTile* act_mtiles = reinterpret_cast<const MTile*>(w + p.mtiles);
+  const int32_t* act_n = reinterpret_cast<const int32_t*>(w + p.n_mtiles);
+  MTile* pipe_mtiles = reinterpret_cast<MTile*>(w + p.pipe_mtiles);
+  int32_t* pipe_n = reinterpret_cast<int32_t*>(w + p.pipe_n_mtiles);
+  err = launch_mtile_list(s, a.offsets, p.pipe_bm, pipe_mtiles, pipe_n, st);
+  if (err != hipSuccess) return err;
+  // dH
+  a.n_ntiles = (s.I + ba::BN - 1) / ba::BN;
+  hipLaunchKernelGGL(ffn_bwd_act_kernel<DH>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(512), 0, st, a,
+                     act_mtiles, act_n);
+  // G and U recomputed on the forward's pipelined gate/up kernel: g*H, dG, dU
+  err = launch_ffn_gate_up_grad(s, x, a.perm_token, w_gate, w_up, GuGrad{a.dh, a.g_row, a.dg, a.du}, a.gh,
+                                pipe_mtiles, a.offsets, pipe_n, p.pipe_mt_max, st);
+  if (err != hipSuccess) return err;
+  // dX
+  a.n_ntiles = (s.d + ba::BN - 1) / ba::BN;
+  hipLaunchKernelGGL(ffn_bwd_act_kernel<DX>, grid_of(size_t(p.mt_max) * a.n_ntiles), dim3(512), 0, st, a,
+                     act_mtiles, act_n);
+  // weight gradients: every expert (an expert without rows gets zero gradients), one
+  // persistent workgroup per CU
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -192,7 +192,7 @@ inline bool grids_fit(const lc_moe_shape& s) {
 // Workspace of lc_moe_ffn_backward (bf16 layers, d and I multiples of 32): the permutation
 // of the given picks (M-tiles of kBmBwd rows), each row's gate, and the row intermediates
 // dH (fp32), g*H, dG, dU (bf16, [T*K][I]) and dX (bf16, [T*K][d]).
-constexpr int kBmBwd = 128;
+constexpr int kBmBwd = 256;
 struct BwPlan {
   size_t block_counts, block_base, load, offsets, mtiles, n_mtiles, done, perm_token, slot_row, g_row,
       dh, gh, dg, du, dxp, pipe_mtiles, pipe_n_mtiles, xp, dyp, zero, total;

@@ -4,7 +4,7 @@ the seeded inputs (gates rounded to fp32), given to both sides.  dx is compared 
 token and dW on every expert (relative L2 per matrix, the bf16 bound 2e-2); experts
 without rows must get exact zeros; two calls give the same bits.  Shapes: one token block
 (T <= 256) and several, ragged N-tiles (d = 160, I = 96), an expert spanning several
-128-row M-tiles, empty experts, Z = 0, all-zero picks; then full-size decode and prefill
+256-row M-tiles, empty experts, Z = 0, all-zero picks; then full-size decode and prefill
 layers (dx on every token, dW on sampled experts incl. the most loaded)."""
 import numpy as np
 import pytest
@@ -68,8 +68,8 @@ def check(case, idx, gate32, out, dy, dw_experts=None):
 
 CASES = [dict(T=300, d=256, N=12, Z=5, K=4, I=192), dict(T=64, d=128, N=8, Z=4, K=3, I=96),
          dict(T=700, d=160, N=6, Z=3, K=3, I=96), dict(T=257, d=64, N=9, Z=0, K=2, I=64),
-         # experts of about 500 rows (four 128-row M-tiles, the last ragged); d and I past
-         # two 128-wide tiles, both ragged
+         # experts of about 500 rows (two 256-row M-tiles, the second ragged); d and I past
+         # one 256-wide tile, both ragged
          dict(T=1500, d=320, N=4, Z=2, K=3, I=288)]
 
 
