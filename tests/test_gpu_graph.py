@@ -13,9 +13,11 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("dtype,T,d,I,wfmt", [("bf16", 64, 512, 256, "rows"), ("bf16", 200, 256, 96, "rows"),
                                               ("f32", 48, 128, 64, "rows"), ("bf16", 64, 512, 256, "packed"),
-                                              ("bf16", 200, 256, 96, "fp8")])
+                                              ("bf16", 200, 256, 96, "fp8"), ("bf16", 200, 256, 128, "fp8act"),
+                                              ("bf16", 300, 256, 192, "fp8act")])
 def test_forward_graph_replay(dtype, T, d, I, wfmt):
-    """wfmt: row-major bf16/fp32 weights, packed bf16 weights, or block-FP8 weights."""
+    """wfmt: row-major bf16/fp32 weights, packed bf16 weights, block-FP8 weights, or block-FP8
+    weights and activations (the FP8 MFMA layer; 64-row and 320-row tile forms)."""
     import torch
     import mixture_experts_layer_router_amd as lm
     wl = adhoc(name=f"graph_{dtype}_{T}_{wfmt}", T=T, d=d, N=24, Z=12, K=6, I=I, dtype=dtype, seed_key=(300, T),
@@ -28,9 +30,9 @@ def test_forward_graph_replay(dtype, T, d, I, wfmt):
     if wfmt == "packed":
         extra = lm.pack_weights(w["gate"], w["up"], w["down"])
         wts = lm._weights(case.w_router, case.bias, None, None, None, None, extra)
-    elif wfmt == "fp8":
+    elif wfmt in ("fp8", "fp8act"):
         extra = lm.quantize_weights(w["gate"], w["up"], w["down"])
-        wts = lm._weights(case.w_router, case.bias, None, None, None, extra)
+        wts = lm._weights(case.w_router, case.bias, None, None, None, extra, None, wfmt == "fp8act")
     else:
         wts = lm._weights(case.w_router, case.bias, w["gate"], w["up"], w["down"])
     dev = case.x.device
@@ -79,6 +81,9 @@ def test_forward_graph_replay(dtype, T, d, I, wfmt):
     if wfmt == "fp8":  # the oracle of the layer on the dequantized weights
         from tests.test_gpu_fp8 import oracle_fp8_forward
         y_ref = oracle_fp8_forward(case)["y"]
+    elif wfmt == "fp8act":  # the oracle of the FP8 MFMA layer
+        from tests.test_gpu_fp8_mfma import act_oracle
+        y_ref = act_oracle(case)["ref"]["y"]
     else:
         y_ref = oracle_forward(case)["y"]
     err = rel_l2(to_np(eager["a"]["y"]), y_ref)
