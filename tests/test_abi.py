@@ -176,6 +176,14 @@ def test_forward_weight_format_validation():
     assert lm.lc_moe_fp8_weights_size(d96) > 0
     assert L.lc_moe_forward(ctypes.byref(d96), P, ctypes.byref(act), P, None, None, None, P,
                             lm.lc_moe_workspace_size(d96), None) == 2
+    # the FP8 MFMA layer addresses its activation matrices with 32-bit offsets: T*K*I < 2^31
+    big = lm.make_shape(1 << 20, 64, 8, 4, 8, 512, lm.BF16)   # T*K*I = 2^32, T*K = 2^23
+    assert lm.lc_moe_workspace_size(big) > 0 and lm.lc_moe_fp8_weights_size(big) > 0
+    assert L.lc_moe_forward(ctypes.byref(big), P, ctypes.byref(act), P, None, None, None, P,
+                            lm.lc_moe_workspace_size(big), None) == 2
+    ok = lm.make_shape(1 << 16, 64, 8, 4, 8, 512, lm.BF16)    # T*K*I = 2^28
+    nb_ok = lm.lc_moe_workspace_size(ok)
+    assert L.lc_moe_forward(ctypes.byref(ok), P, ctypes.byref(act), P, None, None, None, P, nb_ok - 1, None) == 5
 
 
 def test_quantize_activations_validation():
