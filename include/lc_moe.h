@@ -286,7 +286,8 @@ lc_moe_status lc_moe_pack_weights(const lc_moe_shape* shape, const void* w_gate,
  *   dx         [T][d] bf16 (out)
  *   dw_gate, dw_up [N][I][d], dw_down [N][d][I] bf16 (out); an expert without rows gets zeros
  * The workspace (lc_moe_backward_workspace_size; 0 for shapes without a backward) holds the
- * permutation of the picks and the row intermediates (about (T*K) * (12*I + 2*d) bytes). */
+ * permutation of the picks, the x and dy rows gathered in FFN-row order and the row
+ * intermediates: about (T*K) * (10*I + 6*d) bytes. */
 size_t lc_moe_backward_workspace_size(const lc_moe_shape* shape);
 lc_moe_status lc_moe_ffn_backward(const lc_moe_shape* shape, const void* x,
                                   const lc_moe_weights* weights, const int32_t* topk_idx,
