@@ -54,6 +54,21 @@ struct BwArgs {
   int n_ntiles;  // N-tiles per M-tile (dH, dX)
 };
 
+// 4 x 4 transpose among lanes 4q .. 4q+3 of a wave: lane q4 holds column q4 of a block as
+// v[0..3] (rows 0..3) and receives row q4 as w[0..3] (columns 0..3).  Its own v[q4] is
+// column q4; in round s column q4 ^ s comes from lane q4 ^ s, which sends its v[q4].
+__device__ __forceinline__ void quad_transpose(const float (&v)[4], int q4, float (&w)[4]) {
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    float send = v[0];
+#pragma unroll
+    for (int t4 = 1; t4 < 4; ++t4) send = (q4 ^ s4) == t4 ? v[t4] : send;
+    const float got = s4 == 0 ? send : __shfl_xor(send, s4);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) w[c4] = c4 == (q4 ^ s4) ? got : (s4 == 0 ? 0.f : w[c4]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Weight gradients on a persistent direct-load ring: dW_down_e = dY_e^T gH_e and
 // dW_gate_e, dW_up_e = dG_e^T X_e, dU_e^T X_e, the reductions running over the expert's rows.
@@ -264,18 +279,8 @@ __global__ __launch_bounds__(512, 1) void ffn_wgrad_kernel(BwArgs a) {
           float v[4];
 #pragma unroll
           for (int t4 = 0; t4 < 4; ++t4) v[t4] = acc[i][j][rq * 4 + t4];
-          // lane q4 keeps row q4: its own v[q4] is column q4; column q4 ^ s comes from
-          // lane q4 ^ s, which sends its v[q4] (row q4 of its column)
           float w[4];
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) {
-            float send = v[0];
-#pragma unroll
-            for (int t4 = 1; t4 < 4; ++t4) send = (q4 ^ s4) == t4 ? v[t4] : send;
-            const float got = s4 == 0 ? send : __shfl_xor(send, s4);
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) w[c4] = c4 == (q4 ^ s4) ? got : (s4 == 0 ? 0.f : w[c4]);
-          }
+          quad_transpose(v, q4, w);
           const int m = wm * 64 + i * 32 + 8 * rq + 4 * (lane >> 5) + q4;
           const int n = wn * 128 + j * 32 + (lane & 28);
           if (m < Mdim - t.m0 && n < Ndim - t.n0) {
@@ -465,15 +470,7 @@ __global__ __launch_bounds__(512, 1) void ffn_bwd_act_kernel(BwArgs a, const MTi
         float v[4], w[4];
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) v[t4] = acc[i][j][rq * 4 + t4];
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          float send = v[0];
-#pragma unroll
-          for (int t4 = 1; t4 < 4; ++t4) send = (q4 ^ s4) == t4 ? v[t4] : send;
-          const float got = s4 == 0 ? send : __shfl_xor(send, s4);
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) w[c4] = c4 == (q4 ^ s4) ? got : (s4 == 0 ? 0.f : w[c4]);
-        }
+        quad_transpose(v, q4, w);
         const int m = wm * 64 + i * 32 + 8 * rq + 4 * (lane >> 5) + q4;
         const int n = n0 + wn * 128 + j * 32 + (lane & 28);
         if (m < rows && n < ncols) {
