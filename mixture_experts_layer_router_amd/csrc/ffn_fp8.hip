@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "fp8.h"
+#include "lanes.h"
 #include "lds_dma.h"
 
 namespace lcm {
@@ -144,18 +145,33 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
   // one slot per row (four ring stages at d = 6144 instead of three).
   const int sc_bytes = (BM * nkb + 1023) & ~1023;
   __bf16* sc = reinterpret_cast<__bf16*>(smem + LDS_BYTES - sc_bytes);
-  for (int i = tid; i < (BM / 2) * nkb; i += 512) {
-    const int kb = i / (BM / 2), r = 2 * (i - kb * (BM / 2));
-    uint16_t v = 127 | (127 << 8);
-    if (r < rows) {
-      const size_t s0 = MODE == 0 ? size_t(perm_token[row0 + r]) : size_t(row0 + r);
-      v = (v & 0xFF00) | a_scales[s0 * nkb + kb];
+  {
+    // thread = (row pair p, group g of the K blocks kb = g, g + NG, ...): the pair's source
+    // rows are looked up once and its scale bytes read in batches of independent loads, so
+    // the copy waits for a few memory round trips rather than one per slot
+    constexpr int NP = BM / 2, NG = 512 / NP, NB = 8;
+    const int p = tid % NP, g = tid / NP, r = 2 * p;
+    if (g < NG) {
+      const bool v0 = r < rows, v1 = r + 1 < rows;
+      const size_t s0 = !v0 ? 0 : MODE == 0 ? size_t(perm_token[row0 + r]) : size_t(row0 + r);
+      const size_t s1 = !v1 ? 0 : MODE == 0 ? size_t(perm_token[row0 + r + 1]) : size_t(row0 + r + 1);
+      const unsigned char* a0 = a_scales + s0 * nkb;
+      const unsigned char* a1 = a_scales + s1 * nkb;
+      for (int kb0 = g; kb0 < nkb; kb0 += NG * NB) {
+        uint32_t b0[NB], b1[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int kb = kb0 + u * NG;
+          b0[u] = v0 && kb < nkb ? a0[kb] : 127u;
+          b1[u] = v1 && kb < nkb ? a1[kb] : 127u;
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int kb = kb0 + u * NG;
+          if (kb < nkb) sc[kb * NP + p] = __builtin_bit_cast(__bf16, uint16_t(b0[u] | (b1[u] << 8)));
+        }
+      }
     }
-    if (r + 1 < rows) {
-      const size_t s1 = MODE == 0 ? size_t(perm_token[row0 + r + 1]) : size_t(row0 + r + 1);
-      v = (v & 0x00FF) | (uint16_t(a_scales[s1 * nkb + kb]) << 8);
-    }
-    sc[i] = __builtin_bit_cast(__bf16, v);
   }
   // ---- weight scales of the wave's two column blocks (E8M0 = the fp32 exponent field) --
   // lane l holds column block l in vsc[nb][0] and 64 + l in vsc[nb][1] (nkb <= 128)
@@ -238,8 +254,7 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
       const i32x4 lo = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(st + a_lo + mb * 64 * RB));
       const i32x4 hi = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(st + a_hi + mb * 64 * RB));
       fa[buf] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      sa[buf] = (__builtin_bit_cast(uint16_t, sc[kb * (BM / 2) + ((wm * 32 + l32) >> 1) + mb * 32]) >> (8 * (l32 & 1))) &
-                0xFF;
+      sa[buf] = __builtin_bit_cast(uint16_t, sc[kb * (BM / 2) + ((wm * 32 + l32) >> 1) + mb * 32]);  // both rows' bytes
     };
     // B fragments (the lane's pair row, both halves) and their scales: one 16-byte read per
     // 8-element K group holds both halves' 8 bytes.  Lanes l and l + 16 read the same banks,
@@ -282,17 +297,28 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
         if (dma)
           for (int i = 0; i < IA + IB; ++i) issue_one(i, kt + nst, sk);
       } else {
-        rd_b(st, kb);
         rd_a(st, 0, kb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_b(st, kb);
+        // Row block mb: wait for its operands (read one block earlier), issue the next block's
+        // reads, then its two MFMAs.  The compiler's LDS waits cover every read in flight, so
+        // a block's wait has to come before the next block's reads go out: the empty asm that
+        // uses the operands places it there.  The asm after the MFMAs keeps them ahead of the
+        // stage's barrier; without it they sink past the wait's branches, below the barrier,
+        // and every read of a step is issued before any of its MFMAs.
 #pragma unroll
         for (int mb = 0; mb < NV; ++mb) {
           const int cur = mb & 1;
+          asm volatile("" ::"v"(fa[cur]), "v"(fb[0]), "v"(fb[1]), "v"(sa[cur]), "v"(sb[0]), "v"(sb[1]));
+          __builtin_amdgcn_sched_barrier(0);
           if (mb + 1 < NV) rd_a(st, mb + 1, kb, cur ^ 1);  // next row block, beside these MFMAs
           else stage_sync();                                 // the stage's last reads are issued
+          const int sa_row = (sa[cur] >> (8 * (l32 & 1))) & 0xFF;
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[cur], fb[nb], acc[mb][nb], 0, 0, 0,
-                                                                          sa[cur], 0, sb[nb]);
+                                                                          sa_row, 0, sb[nb]);
+          asm volatile("" : "+v"(acc[mb][0]), "+v"(acc[mb][1]));
           // keep the scheduler from hoisting every row block's reads (registers for two only)
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -318,6 +344,9 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
 
   // ---- epilogue; 32x32 D layout: column lane & 31, rows 8*(r/4) + 4*(lane/32) + r%4 --------
   if constexpr (MODE == 1) {
+    // one bf16 per lane and accumulator: a 4-lane transpose into 8-byte stores (as for H
+    // below) made this kernel slower, its 32 K steps per unit being too few to carry the
+    // transposes
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= nvb) continue;
@@ -334,7 +363,14 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
     }
   } else {
     // H = silu(G) U; its block of this row is the n-tile's 128 columns, spread over the 4
-    // column waves (32 lanes each): lane maxima -> half-wave maxima -> LDS -> row maximum
+    // column waves (32 lanes each).  Row maxima over a wave's 32 columns: a butterfly over
+    // lane bits 4..0 that halves the rows a lane carries at each step, so that lane l ends
+    // with the maximum of accumulator index (l & 31) >> 1; then LDS and the 4 column waves.
+    // The codes go out through a 4-lane transpose: each lane gets 4 adjacent columns of one
+    // row (row 8 rq + 4 h + q4 of the row block for accumulators 4 rq .. 4 rq + 3) and stores
+    // them as one 4-byte piece; column counts are multiples of 64, so a piece is in range or
+    // out of it as a whole.
+    const int q4 = lane & 3;
     const int col = n0 + wn * 32 + l32;
     const bool cin = col < ncols;
     __syncthreads();  // every wave is done with the ring
@@ -342,30 +378,50 @@ __global__ __launch_bounds__(512, SMALL ? 2 : 1) void ffn_fp8_mfma_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= nvb) continue;
+      float m[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float hv = cin ? swiglu_fast(acc[mb][0][r], acc[mb][1][r]) : 0.f;
         acc[mb][0][r] = hv;
-        float m = fabsf(hv);
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));  // within the half
-        const int row = (mb * 2 + wm) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (l32 == 0) pmax[wn * BM + row] = m;
+        m[r] = fabsf(hv);
       }
+#pragma unroll
+      for (int step = 0, half = 8; step < 4; ++step, half >>= 1) {  // lane bits 4, 3, 2, 1
+        const bool b = (l32 >> (4 - step)) & 1;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          const float keep = b ? m[i + half] : m[i];
+          const float send = b ? m[i] : m[i + half];
+          m[i] = fmaxf(keep, __shfl_xor(send, 16 >> step));
+        }
+      }
+      const float rmax = fmaxf(m[0], __shfl_xor(m[0], 1));
+      const int ri = l32 >> 1;
+      if ((l32 & 1) == 0) pmax[wn * BM + (mb * 2 + wm) * 32 + 8 * (ri >> 2) + 4 * h + (ri & 3)] = rmax;
     }
     __syncthreads();
     const int nkbh = (ncols + 127) / 128;
+    const int colq = n0 + wn * 32 + (l32 & 28);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= nvb) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (mb * 2 + wm) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int rq = 0; rq < 4; ++rq) {
+        float v[4], w[4];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) v[t4] = acc[mb][0][rq * 4 + t4];
+        quad_transpose(v, q4, w);
+        const int row = (mb * 2 + wm) * 32 + 8 * rq + 4 * h + q4;
         if (row >= rows) continue;
         const float amax = fmaxf(fmaxf(pmax[row], pmax[BM + row]), fmaxf(pmax[2 * BM + row], pmax[3 * BM + row]));
         const int k = block_exp(amax);
-        if (cin) hq[size_t(row0 + row) * ncols + col] = static_cast<unsigned char>(e4m3_code(ldexpf(acc[mb][0][r], -k)));
-        if (wn == 0 && l32 == 0) hs[size_t(row0 + row) * nkbh + ntile] = static_cast<unsigned char>(k + 127);
+        if (colq < ncols) {
+          uint32_t c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c |= e4m3_code(ldexpf(w[j], -k)) << (8 * j);
+          *reinterpret_cast<uint32_t*>(hq + size_t(row0 + row) * ncols + colq) = c;
+        }
+        if (wn == 0 && l32 < 4) hs[size_t(row0 + row) * nkbh + ntile] = static_cast<unsigned char>(k + 127);
       }
     }
   }
