@@ -10,10 +10,13 @@
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E4M3 codes and applies one E8M0 scale per row
 // (A) or column (B) and 32-element K block, taking the scale of row m's K block kb from lane
-// m + 32 kb; the products are exact and the sums fp32, so the MFMA computes exactly the
-// dequantized operands' dot product.  Every scale here covers 128 K elements, so lanes m and
-// m + 32 pass the same scale and each lane may hold any 32 of its row's 64 K codes as long as
-// A and B agree: lane l (half h = l / 32) holds K h*32 .. h*32 + 31 of the stage.
+// m + 32 kb.  The products are exact (the dequantized operands' products), but the sums are
+// not fp32-exact: the instruction adds its 64 products and the accumulator with about 12
+// bits below the largest addend, so a chained K loop carries errors up to about
+// 2^-13 (|G| + rss of G's products), measured.  Every scale here covers 128 K elements, so
+// lanes m and m + 32 pass the same scale and each lane may hold any 32 of its row's 64 K
+// codes as long as A and B agree: lane l (half h = l / 32) holds K h*32 .. h*32 + 31 of the
+// stage.
 //
 // A 64-element K stage of FP8 codes is 64 bytes per row, the same bytes as a 32-element
 // bf16 stage, so the ring, the direct global->LDS loads, the waits and the XCD-aware unit

@@ -9,22 +9,29 @@
     scale blocks per row in either projection, and one token;
   * at full size: sampled prefill tokens, and the whole first 320-row tile of the skewed
     layer's most loaded expert.
-The weights-only FP8 layer fails the same per-token bound (so the activations are seen to
-be quantized).
+The weights-only FP8 layer is at least 2 times farther from the reference than the FP8
+MFMA layer (12 times on most shapes, 2.5 with I = 64: the activations are seen to be
+quantized).
 
 Tolerance.  The kernel's arithmetic differs from the oracle's in three places: G and U are
-fp32 sums (the products of FP8 codes and power-of-two scales are exact), Y rows and the
-output are rounded to bf16, and H = silu(G) U is formed in fp32 before it is quantized.
-The first two move a token's output by at most 2^-9 (||y_t|| + sum_k g_k ||Y_k||), taken
-with a factor 2 of margin.  The third matters where H lies next to an E4M3 rounding
-boundary: there the kernel's fp32 H and the oracle's fp64 H may take neighbouring codes,
-a step of 6-12% of that element.  Each H element's fp32 uncertainty is modelled as
-  eG = 16 u sqrt(d/64) (|G| + rss(G terms)), eU alike (one fp32 rounding per 64-element
-  stage of the accumulation, 16 standard deviations), eH = |U silu'(G)| eG +
-  |silu(G)| eU + 8 u |H|,   u = 2^-24,
+sums formed by the FP8 matrix cores (the products of FP8 codes and power-of-two scales are
+exact, the sums are not fp32-exact, see below), Y rows and the output are rounded to bf16,
+and H = silu(G) U is formed in fp32 before it is quantized.  Rounding Y and y moves a
+token's output by at most 2^-9 (||y_t|| + sum_k g_k ||Y_k||), taken with a factor 2 of
+margin.  Where H lies next to an E4M3 rounding boundary, the kernel's H and the oracle's
+fp64 H may take neighbouring codes, a step of 6-12% of that element.  The scaled FP8 MFMA
+adds its 64 products and the accumulator with about 12 bits below the largest addend: run
+as the K loop runs it (1 to 96 steps into one accumulator, operands spread like
+block-quantized data), its error stayed below 2^-13 (|G| + rss(G's products)) over 262144
+sums per length, far above one fp32 rounding per step.  So each H element's uncertainty is
+  eG = 2^-11 (|G| + rss(G terms)), eU alike (4 times the largest error seen),
+  eH = |U silu'(G)| eG + |silu(G)| eU + 8 u |H|,   u = 2^-24,
 and oracle.fp8.rows_requant_bound turns it into the largest move of each quantized H
 element; a token may differ by sum_k g_k sum_i delta_ki ||W_down[:, i]|| more.  Elements
-away from a boundary have delta = 0, so a wrong code there still fails."""
+away from a boundary have delta = 0, so a wrong code there still fails.  That per-token
+bound is sound but loose (it lets every element near a boundary move); the layer's error
+pooled over all checked tokens must also stay within 2^-7, where the real code changes,
+rare and independent, leave it near the bf16 rounding level (about 2e-3)."""
 import collections
 import concurrent.futures
 
@@ -35,9 +42,15 @@ from inputs import configs
 from inputs.generate import weights_f64
 from oracle import fp8 as ofp8
 from oracle import moe as orc
-from tests.gpu_common import BF16_TOL, U32, adhoc, audited, make_case, rel_l2, say, to_np, worst_token_rel
+from tests.gpu_common import U32, adhoc, audited, make_case, rel_l2, say, to_np, worst_token_rel
 
 pytestmark = pytest.mark.gpu
+
+# Accumulation error of the FP8 matrix cores, relative to |G| + rss(G's products): 4 times
+# the largest seen when chaining 1 to 96 scaled FP8 MFMAs (64 K each) into one accumulator.
+MFMA_ACC = 2.0 ** -11
+# Relative L2 error of the layer pooled over the checked tokens (bf16 rounding is about 2e-3).
+POOLED_TOL = 2.0 ** -7
 
 
 def _lm():
@@ -75,9 +88,8 @@ def audited_expert(rows):
     def fn(X, wg, wu, wd):
         Y = ofp8.fp8_act_expert(X, wg, wu, wd)
         Xq, G, U, H = ofp8.fp8_act_hidden(X, wg, wu)
-        stages = np.sqrt(X.shape[1] / 64)
-        eG = 16 * U32 * stages * (np.abs(G) + np.sqrt((Xq ** 2) @ (wg ** 2).T))
-        eU = 16 * U32 * stages * (np.abs(U) + np.sqrt((Xq ** 2) @ (wu ** 2).T))
+        eG = MFMA_ACC * (np.abs(G) + np.sqrt((Xq ** 2) @ (wg ** 2).T))
+        eU = MFMA_ACC * (np.abs(U) + np.sqrt((Xq ** 2) @ (wu ** 2).T))
         s = expit(G)
         eH = np.abs(U * s * (1 + G * (1 - s))) * eG + np.abs(G * s) * eU + 8 * U32 * np.abs(H)
         delta = ofp8.rows_requant_bound(H, eH)
@@ -122,7 +134,7 @@ def check_layer(got_y, got_idx, o, label):
     bad = np.nonzero(dev > o["base"] + o["allow"])[0]
     assert bad.size == 0, (f"{label}: tokens {bad[:5]} off by {dev[bad[:5]]} > "
                            f"{o['base'][bad[:5]]} + {o['allow'][bad[:5]]}")
-    assert err <= BF16_TOL
+    assert err <= POOLED_TOL, (label, err)
     return err
 
 
@@ -156,13 +168,12 @@ def test_forward_fp8_act_matches_oracle(T, d, I, N, Z, K):
     q = lm.quantize_weights(case.w["gate"], case.w["up"], case.w["down"])
     got = run(case, q)
     o = act_oracle(case)
-    check_layer(got["y"], got["topk_idx"], o, "layer")
-    # the weights-only FP8 layer (x and H in bf16) fails the same per-token bound
+    err = check_layer(got["y"], got["topk_idx"], o, "layer")
+    # the weights-only FP8 layer (x and H in bf16) is much farther from this reference
     w8 = run(case, q, fp8_act=False)
-    dev8 = np.linalg.norm(w8["y"] - o["ref"]["y"], axis=1)
-    n_off = int((dev8 > o["base"] + o["allow"]).sum())
-    say(f"  weights-only FP8 layer vs it: rel L2 {rel_l2(w8['y'], o['ref']['y']):.2e}, {n_off} tokens off")
-    assert n_off > 0
+    err8 = rel_l2(w8["y"], o["ref"]["y"])
+    say(f"  weights-only FP8 layer vs it: rel L2 {err8:.2e} ({err8 / err:.1f} times the FP8 MFMA layer's)")
+    assert err8 >= 2 * err
     # deterministic
     again = run(case, q)
     assert np.array_equal(again["y"], got["y"])
