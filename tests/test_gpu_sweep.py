@@ -1,0 +1,82 @@
+"""Seeded random shapes through every path each shape admits, against the fp64 oracle.
+
+The shapes are drawn once from a fixed seed within the header's limits: bf16 (d and I
+multiples of 8, half of them multiples of 64) and fp32 (multiples of 4), 1 to 64 FFN
+experts, 0 to 20 zero experts, K from 1 to 8, T from 1 to 2500 (one token block or
+several, the 64-row and 320-row tile forms, experts over several M-tiles).  Each shape runs:
+  * the layer on row-major weights: picks bit-exact, output within the bf16 (fp32) bound
+    per token and pooled;
+  * for d and I multiples of 32: the layer on packed weights and on block-FP8 weights, and
+    the FFN backward (dx per token, dW per expert);
+  * for d and I multiples of 64: the FP8 MFMA layer (FP8 activations).
+The checks are those of the dedicated tests (test_gpu_parity, test_gpu_packed,
+test_gpu_fp8, test_gpu_fp8_mfma, test_gpu_backward); this file adds the breadth of shapes.
+Routing inputs are audited as everywhere (near-tie tokens redrawn)."""
+import numpy as np
+import pytest
+
+from tests import test_gpu_backward as tb
+from tests import test_gpu_fp8 as t8
+from tests import test_gpu_fp8_mfma as tm
+from tests.gpu_common import BF16_TOL, F32_TOL, adhoc, audited, make_case, oracle_forward, rel_l2, say, to_np, \
+    worst_token_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = "f32" if rng.random() < 0.15 else "bf16"
+        unit = 4 if dtype == "f32" else (64 if rng.random() < 0.5 else 8)
+        d = int(unit * rng.integers(1, max(2, 640 // unit)))
+        I = int(unit * rng.integers(1, max(2, 640 // unit)))
+        N = int(rng.choice([1, 2, 3, 5, 8, 12, 17, 33, 64]))
+        Z = int(rng.choice([0, 0, 1, 2, 5, 9, 20]))
+        K = int(rng.integers(1, min(8, N + Z) + 1))
+        T = int(rng.choice([1, 2, 3, 7, 31, 64, 65, 100, 255, 256, 257, 300, 513, 700, 1000, 1600, 2500]))
+        out.append((dtype, T, d, I, N, Z, K))
+    return out
+
+
+SHAPES = _shapes()
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES)), ids=lambda i: "{}_T{}_d{}_I{}_N{}_Z{}_K{}".format(*SHAPES[i]))
+def test_random_shape(i):
+    import mixture_experts_layer_router_amd as lm
+    dtype, T, d, I, N, Z, K = SHAPES[i]
+    say(f"[sweep {i}] {dtype} T={T} d={d} I={I} N={N} Z={Z} K={K}")
+    wl = adhoc(name=f"sweep{i}", T=T, d=d, N=N, Z=Z, K=K, I=I, dtype=dtype, seed_key=(910, i, T, d, I),
+               expert_std=1 / np.sqrt(d), bias=("uniform", 0.5 / (N + Z)))
+    case = make_case(wl, ri=audited(wl))
+    ref = oracle_forward(case)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    out = lm.forward(case.x, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], K)
+    np.testing.assert_array_equal(out["topk_idx"].cpu().numpy(), ref["idx"])
+    y = to_np(out["y"])
+    err, worst = rel_l2(y, ref["y"]), worst_token_rel(y, ref["y"])
+    say(f"   layer rel L2 {err:.2e} (worst token {worst:.2e})")
+    assert err <= tol and (dtype == "f32" or worst <= tol)
+    if dtype != "bf16" or d % 32 or I % 32:
+        return
+    p = lm.pack_weights(case.w["gate"], case.w["up"], case.w["down"])
+    yp = to_np(lm.forward(case.x, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], K,
+                         packed=p)["y"])
+    assert rel_l2(yp, ref["y"]) <= BF16_TOL and worst_token_rel(yp, ref["y"]) <= BF16_TOL
+    del p
+    q = lm.quantize_weights(case.w["gate"], case.w["up"], case.w["down"])
+    y8 = to_np(lm.forward(case.x, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], K,
+                         fp8=q)["y"])
+    r8 = t8.oracle_fp8_forward(case)
+    e8 = rel_l2(y8, r8["y"])
+    say(f"   FP8-weight layer rel L2 {e8:.2e}")
+    assert e8 <= BF16_TOL
+    if d % 64 == 0 and I % 64 == 0:
+        got = tm.run(case, q)
+        tm.check_layer(got["y"], got["topk_idx"], tm.act_oracle(case), "   FP8 MFMA layer")
+    del q
+    idx, gate32 = tb.routing(case)
+    bo, dy = tb.run_backward(case, idx, gate32)
+    tb.check(case, idx, gate32, bo, dy)
