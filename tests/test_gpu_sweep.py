@@ -5,7 +5,8 @@ multiples of 8, half of them multiples of 64) and fp32 (multiples of 4), 1 to 64
 experts, 0 to 20 zero experts, K from 1 to 8, T from 1 to 2500 (one token block or
 several, the 64-row and 320-row tile forms, experts over several M-tiles).  Each shape runs:
   * the layer on row-major weights: picks bit-exact, output within the bf16 (fp32) bound
-    per token and pooled;
+    per token and pooled; the permutation of the oracle's picks exact; the staged and the
+    allocation-free forwards bitwise equal to it;
   * for d and I multiples of 32: the layer on packed weights and on block-FP8 weights, and
     the FFN backward (dx per token, dW per expert);
   * for d and I multiples of 64: the FP8 MFMA layer (FP8 activations).
@@ -18,6 +19,7 @@ import pytest
 from tests import test_gpu_backward as tb
 from tests import test_gpu_fp8 as t8
 from tests import test_gpu_fp8_mfma as tm
+from oracle import moe as orc
 from tests.gpu_common import BF16_TOL, F32_TOL, adhoc, audited, make_case, oracle_forward, rel_l2, say, to_np, \
     worst_token_rel
 
@@ -59,6 +61,8 @@ def test_random_shape(i):
     err, worst = rel_l2(y, ref["y"]), worst_token_rel(y, ref["y"])
     say(f"   layer rel L2 {err:.2e} (worst token {worst:.2e})")
     assert err <= tol and (dtype == "f32" or worst <= tol)
+    _check_permute(case, ref["idx"])
+    _check_same_bits(case, out)
     if dtype != "bf16" or d % 32 or I % 32:
         return
     p = lm.pack_weights(case.w["gate"], case.w["up"], case.w["down"])
@@ -80,3 +84,46 @@ def test_random_shape(i):
     idx, gate32 = tb.routing(case)
     bo, dy = tb.run_backward(case, idx, gate32)
     tb.check(case, idx, gate32, bo, dy)
+
+
+def _check_permute(case, ridx):
+    """lc_moe_permute on the oracle's picks: offsets, permutation and slots exact, the rows
+    past the FFN rows untouched, the gathered rows bit-exact."""
+    import torch
+    import mixture_experts_layer_router_amd as lm
+    wl = case.wl
+    out = lm.permute(case.x, torch.from_numpy(ridx.astype(np.int32)).to(case.x.device), wl.N, wl.E)
+    offsets, perm_token, slot_row = orc.permute(ridx, wl.N)
+    nnz = int(offsets[-1])
+    assert (to_np(out["ffn_offsets"]) == offsets).all()
+    pt = to_np(out["perm_token"])
+    assert (pt[:nnz] == perm_token).all() and (pt[nnz:] == -7).all()
+    assert (to_np(out["slot_row"]) == slot_row).all()
+    assert (to_np(out["load"]) == orc.expert_load(ridx, wl.E)).all()
+    xp, xr = out["x_perm"][:nnz], case.x[torch.from_numpy(perm_token).to(case.x.device)]
+    assert torch.equal(xp.view(torch.int16), xr.view(torch.int16)) if xp.dtype == torch.bfloat16 else torch.equal(xp, xr)
+
+
+def _check_same_bits(case, out):
+    """The staged forward and (where the shape fits its array) the allocation-free forward
+    give the plain forward's bits."""
+    import torch
+    import mixture_experts_layer_router_amd as lm
+    wl = case.wl
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(lm.NUM_STAGES + 1)]
+    for e in events:  # torch creates the HIP event on its first record
+        e.record()
+    st = lm.forward(case.x, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], wl.K,
+                    stage_events=events)
+    torch.cuda.synchronize()
+    for k in out:
+        assert torch.equal(st[k], out[k]), ("staged", k)
+    shape = lm.make_shape(wl.T, wl.d, wl.N, wl.Z, wl.K, wl.I, lm.BF16 if wl.dtype == "bf16" else lm.F32)
+    if lm.lc_moe_workspace_size(shape) > lm.STATIC_WORKSPACE_BYTES:
+        return
+    na = {k: torch.empty_like(v) for k, v in out.items()}
+    wts = lm._weights(case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"])
+    lm.lc_moe_forward_noalloc(shape, case.x, wts, na["y"], na["topk_idx"], na["topk_gate"], na["load"])
+    torch.cuda.synchronize()
+    for k in out:
+        assert torch.equal(na[k], out[k]), ("noalloc", k)
