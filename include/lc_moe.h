@@ -227,8 +227,10 @@ lc_moe_status lc_moe_quantize_weights(const lc_moe_shape* shape, const void* w_g
  * partial) gets the scale 2^k, k the smallest integer with the block's max |v| <= 448 * 2^k
  * (k = 0 for an all-zero block), stored as the E8M0 byte k + 127; each v / 2^k rounds to
  * the nearest E4M3 code, ties to the even code.  The layer computed with fp8_act is then
- *   G = Q(x) Q(W_gate)^T, U = Q(x) Q(W_up)^T (exact products of dequantized values, fp32
- *   sums), H = silu(G) U (fp32), Y = Q(H) Q(W_down)^T rounded to bf16,
+ *   G = Q(x) Q(W_gate)^T, U = Q(x) Q(W_up)^T (exact products of dequantized values, summed
+ *   by the FP8 matrix cores: about 12 bits below the largest addend per 64-element step,
+ *   so G and U may be off by about 2^-13 (|G| + rss of the products), not fp32-exact),
+ *   H = silu(G) U (fp32), Y = Q(H) Q(W_down)^T rounded to bf16,
  * combined as the bf16 layer's Y is.  Blocks whose max |v| is nonzero but below
  * 448 * 2^-127 are outside the contract.
  *   x       [rows][cols] bf16
