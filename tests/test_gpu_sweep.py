@@ -6,7 +6,8 @@ experts, 0 to 20 zero experts, K from 1 to 8, T from 1 to 2500 (one token block 
 several, the 64-row and 320-row tile forms, experts over several M-tiles).  Each shape runs:
   * the layer on row-major weights: picks bit-exact, output within the bf16 (fp32) bound
     per token and pooled; the permutation of the oracle's picks exact; the staged and the
-    allocation-free forwards bitwise equal to it;
+    allocation-free forwards, and replays of the forward captured in a HIP graph (two input
+    sets in turn, eager work between replays), bitwise equal to it;
   * for d and I multiples of 32: the layer on packed weights and on block-FP8 weights, and
     the FFN backward (dx per token, dW per expert);
   * for d and I multiples of 64: the FP8 MFMA layer (FP8 activations).
@@ -63,6 +64,7 @@ def test_random_shape(i):
     assert err <= tol and (dtype == "f32" or worst <= tol)
     _check_permute(case, ref["idx"])
     _check_same_bits(case, out)
+    _check_graph(case, out)
     if dtype != "bf16" or d % 32 or I % 32:
         return
     p = lm.pack_weights(case.w["gate"], case.w["up"], case.w["down"])
@@ -127,3 +129,41 @@ def _check_same_bits(case, out):
     torch.cuda.synchronize()
     for k in out:
         assert torch.equal(na[k], out[k]), ("noalloc", k)
+
+
+def _check_graph(case, out):
+    """The forward captured in a graph and replayed on two input sets in turn, with eager
+    forwards on the same workspace between replays: every replay gives the eager bits."""
+    import torch
+    import mixture_experts_layer_router_amd as lm
+    wl = case.wl
+    shape = lm.make_shape(wl.T, wl.d, wl.N, wl.Z, wl.K, wl.I, lm.BF16 if wl.dtype == "bf16" else lm.F32)
+    ws = lm.workspace_for(shape, case.x.device)
+    wts = lm._weights(case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"])
+    x_static, x_other = case.x.clone(), (case.x.float() * -0.5).to(case.x.dtype)
+    g_out = {k: torch.empty_like(v) for k, v in out.items()}
+    eager_other = lm.forward(x_other, case.w_router, case.bias, case.w["gate"], case.w["up"], case.w["down"], wl.K)
+
+    def fwd(x, o):
+        lm.lc_moe_forward(shape, x, wts, o["y"], o["topk_idx"], o["topk_gate"], o["load"], ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        fwd(x_static, g_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(x_static, g_out)
+    torch.cuda.synchronize()
+    for rep, (src, want) in enumerate(((case.x, out), (x_other, eager_other), (case.x, out))):
+        for v in g_out.values():
+            v.zero_()
+        x_static.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in g_out:
+            assert torch.equal(g_out[k], want[k]), ("graph", rep, k)
+        fwd(x_other, {k: torch.empty_like(v) for k, v in out.items()})  # eager work in between
+        torch.cuda.synchronize()
