@@ -37,6 +37,9 @@
  *     inputs are outside the contract.
  *   - Results are deterministic: two calls with the same inputs give bitwise equal
  *     outputs (no floating-point atomics anywhere).
+ *   - The header is C (C99 and later) and C++.  It takes hipStream_t from
+ *     <hip/hip_runtime_api.h>, which needs __HIP_PLATFORM_AMD__ defined (hipcc defines it;
+ *     a plain C or C++ compiler takes -D__HIP_PLATFORM_AMD__ -I<ROCm>/include).
  *   - Limits: T, d, N, K, I >= 1; Z >= 0; K <= N+Z; N+Z <= 4096; N <= 2048;
  *     d and I multiples of 8 for bf16 (4 for fp32); and every kernel launch of the shape
  *     within the device's grid (at most 2^32 - 1 work-items along x): this needs
